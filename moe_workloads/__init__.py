@@ -1,0 +1,225 @@
+"""Seeded synthetic inputs for one mixture-of-experts SwiGLU layer forward.
+
+This module only draws random numbers, rounds them to bf16 and names the
+workload shapes.  It holds none of the layer's arithmetic, so both the CPU
+oracle (``oracle/``) and the HIP path's tests and benchmark can take their
+inputs from it without sharing any of the method's code.
+
+Shapes follow the pages this project builds from:
+  * "Mixture of Experts in vLLM -- From First Principles to fused_moe",
+    section "One expert, and one token": x has H values, the stacked gate/up
+    matrix W13 is [2I, H] (gate rows first), the down matrix W2 is [H, I],
+    the router W_r is [E, H].
+  * same page, "A batch: (token, expert) pairs": the toy batch has M=3
+    tokens, 4 experts and top_k=2.
+  * "MoE Execution Path Analysis", "The Real Bottleneck": 256 experts with
+    top-8 routing (the wide layer below keeps that routing shape).
+
+Value distributions (the readings are stated in the design doc):
+  x ~ N(0, 1); W13 ~ N(0, 1/H) and W2 ~ N(0, 1/I) (variance 1/fan-in);
+  W_r ~ N(0, 0.02^2) for the model-shaped layers and N(0, 1/H) for the toy.
+  Every tensor is drawn in float32 and rounded once, round-to-nearest-even,
+  to bf16; all consumers see the same bf16 bit patterns.
+  The skewed prefill layer adds a Zipf(s=1.1) prior to the router logits:
+  bias[e] = -1.1 * ln(rank[e]) with rank a seeded permutation of 1..E.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+SEED_BASE = 20261202
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    name: str
+    index: int          # position in the workload list; enters the seed
+    E: int              # experts
+    top_k: int          # experts per token
+    H: int              # hidden size (GEMM 1 K, GEMM 2 N)
+    I: int              # expert intermediate size (GEMM 2 K)
+    Ms: tuple           # token counts exercised for this shape
+    router_std: Optional[float]   # None -> 1/sqrt(H)
+    zipf_s: Optional[float] = None
+    renormalize: bool = True
+    description: str = ""
+
+
+WORKLOADS = {
+    "toy": LayerShape(
+        "toy", 0, E=4, top_k=2, H=64, I=32, Ms=(3,), router_std=None,
+        description="toy layer: M=3, E=4, top_k=2, H=64, I=32"),
+    "qwen3_decode": LayerShape(
+        "qwen3_decode", 1, E=128, top_k=8, H=2048, I=768, Ms=(1, 2, 8, 16, 64),
+        router_std=0.02,
+        description="Qwen3-30B-A3B-shaped MoE layer, decode batches M=1..64"),
+    "qwen3_prefill": LayerShape(
+        "qwen3_prefill", 2, E=128, top_k=8, H=2048, I=768, Ms=(4096,),
+        router_std=0.02, zipf_s=1.1,
+        description="Qwen3-30B-A3B-shaped MoE layer, prefill M=4096, "
+                    "Zipf(1.1)-biased router"),
+    "qwen15": LayerShape(
+        "qwen15", 3, E=60, top_k=4, H=2048, I=1408, Ms=(1, 16, 512, 2048),
+        router_std=0.02,
+        description="Qwen1.5-MoE-A2.7B-shaped MoE layer (down-proj K=1408)"),
+    "wide256": LayerShape(
+        "wide256", 4, E=256, top_k=8, H=2048, I=512, Ms=(1, 8, 8192),
+        router_std=0.02,
+        description="256-expert wide layer, top-8"),
+}
+
+
+def seed_for(shape: LayerShape, M: int, layer: int = 0) -> int:
+    """Seed of one synthetic layer; ``layer`` > 0 names extra timing layers."""
+    return SEED_BASE + 100 * shape.index + M + 1_000_003 * layer
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even).
+
+    Returns the bf16 bit patterns as uint16.  Inputs here are finite.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_bf16_into(out: np.ndarray, seq: np.random.SeedSequence,
+                     std: float) -> None:
+    """Fill ``out`` (uint16) with bf16(N(0, std^2)) drawn from stream ``seq``."""
+    rng = np.random.Generator(np.random.PCG64(seq))
+    v = rng.standard_normal(out.shape, dtype=np.float32)
+    if std != 1.0:
+        v *= np.float32(std)
+    u = v.view(np.uint32)
+    u += ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    u >>= np.uint32(16)
+    out[...] = u
+
+
+def make_layer(shape: LayerShape | str, M: int, layer: int = 0,
+               E: Optional[int] = None, top_k: Optional[int] = None,
+               H: Optional[int] = None, I: Optional[int] = None,
+               seed: Optional[int] = None) -> dict:
+    """Draw one synthetic MoE layer and a batch of M tokens.
+
+    Returns a dict with numpy arrays
+      x          uint16 [M, H]       bf16 bits
+      w_router   uint16 [E, H]       bf16 bits
+      w13        uint16 [E, 2I, H]   bf16 bits, gate rows 0..I-1, up rows I..2I-1
+      w2         uint16 [E, H, I]    bf16 bits
+      logit_bias float32 [E] or None
+    and the scalars M, E, top_k, H, I, renormalize.
+    E/top_k/H/I may be overridden to make small cases of the same recipe.
+    Streams: numpy SeedSequence(seed).spawn(2 + 2E + 1) gives one PCG64
+    stream each to x, W_r, W13[e] (e = 0..E-1), W2[e], and the Zipf rank
+    permutation, in that order; tensors are independent of thread order.
+    """
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    E = shape.E if E is None else E
+    top_k = shape.top_k if top_k is None else top_k
+    H = shape.H if H is None else H
+    I = shape.I if I is None else I
+    seqs = np.random.SeedSequence(
+        seed_for(shape, M, layer) if seed is None else seed).spawn(2 + 2 * E + 1)
+    rstd = shape.router_std if shape.router_std is not None else 1.0 / math.sqrt(H)
+    x = np.empty((M, H), dtype=np.uint16)
+    w_router = np.empty((E, H), dtype=np.uint16)
+    w13 = np.empty((E, 2 * I, H), dtype=np.uint16)
+    w2 = np.empty((E, H, I), dtype=np.uint16)
+    jobs = [(x, seqs[0], 1.0), (w_router, seqs[1], rstd)]
+    jobs += [(w13[e], seqs[2 + e], 1.0 / math.sqrt(H)) for e in range(E)]
+    jobs += [(w2[e], seqs[2 + E + e], 1.0 / math.sqrt(I)) for e in range(E)]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    if workers == 1 or w13.size < (1 << 20):
+        for job in jobs:
+            _normal_bf16_into(*job)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda j: _normal_bf16_into(*j), jobs))
+    bias = None
+    if shape.zipf_s is not None:
+        rank = np.random.Generator(np.random.PCG64(seqs[-1])).permutation(E) + 1
+        bias = (-shape.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
+    return dict(x=x, w_router=w_router, w13=w13, w2=w2, logit_bias=bias,
+                M=M, E=E, top_k=top_k, H=H, I=I,
+                renormalize=shape.renormalize, name=shape.name)
+
+
+def make_topk_ids(M: int, top_k: int, E: int, seed: int,
+                  pattern: str = "random") -> np.ndarray:
+    """Synthetic expert choices [M, top_k] int32 for testing the align step.
+
+    Patterns: "random" (distinct ids per token, uniform), "one_expert_heavy"
+    (every token takes expert 0 in some slot), "round_robin"
+    (token t takes experts (t*top_k + j) mod E), "sparse" (only a few
+    experts are ever chosen, so most experts are empty).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids = np.empty((M, top_k), dtype=np.int32)
+    if pattern == "round_robin":
+        for t in range(M):
+            ids[t] = (t * top_k + np.arange(top_k)) % E
+        return ids
+    if pattern == "sparse":
+        pool = rng.choice(E, size=min(E, max(top_k, 2 * top_k)), replace=False)
+        for t in range(M):
+            ids[t] = rng.choice(pool, size=top_k, replace=False)
+        return ids
+    for t in range(M):
+        ids[t] = rng.choice(E, size=top_k, replace=False)
+    if pattern == "one_expert_heavy":
+        for t in range(M):
+            if 0 not in ids[t]:
+                ids[t, rng.integers(top_k)] = 0
+    return ids
+
+
+def make_device_layer(shape: LayerShape | str, M: int, layer: int, device,
+                      E: Optional[int] = None, I: Optional[int] = None):
+    """Draw the weights of one extra timing layer directly in device memory.
+
+    Same distributions as :func:`make_layer` but drawn with torch's seeded
+    generator on the device (a different stream of numbers), so a benchmark
+    can cycle through many distinct layers without host-side generation.
+    Returns a dict of torch tensors (bf16) w_router, w13, w2 and logit_bias.
+    """
+    import torch  # local import: the oracle side never needs torch
+
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    E = shape.E if E is None else E
+    I = shape.I if I is None else I
+    H = shape.H
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(shape, M, layer))
+    rstd = shape.router_std if shape.router_std is not None else 1.0 / math.sqrt(H)
+
+    def draw(sz, std):
+        t = torch.randn(sz, generator=g, device=device, dtype=torch.float32)
+        t.mul_(std)
+        return t.to(torch.bfloat16)
+
+    w_router = draw((E, H), rstd)
+    w13 = draw((E, 2 * I, H), 1.0 / math.sqrt(H))
+    w2 = draw((E, H, I), 1.0 / math.sqrt(I))
+    bias = None
+    if shape.zipf_s is not None:
+        rank = torch.randperm(E, generator=g, device=device).to(torch.float64) + 1
+        bias = (-shape.zipf_s * torch.log(rank)).to(torch.float32)
+    return dict(w_router=w_router, w13=w13, w2=w2, logit_bias=bias)

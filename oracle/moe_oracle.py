@@ -1,0 +1,260 @@
+"""Plain, slow, obviously correct CPU oracle of one MoE SwiGLU layer forward.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the HIP library never
+calls this module, and this module never imports the HIP library.
+
+All floating point is float64 on bf16 inputs widened exactly.  The one place
+where floating point decides an integer -- which experts a token keeps -- is
+taken on float32 logits, the precision the GPU kernel decides in; the
+probabilities and weights themselves are computed in float64.
+
+Sources (page title, then section):
+  [MoE-vLLM] "Mixture of Experts in vLLM - From First Principles to fused_moe"
+  [Exec]     "MoE Execution Path Analysis"
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half
+    of an IEEE float32)."""
+    b = np.ascontiguousarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# routing: [MoE-vLLM] "One expert, and one token", sub-section
+# "One token uses only 8 experts"
+# ---------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  logit_bias: np.ndarray | None = None) -> np.ndarray:
+    """Router scores: one linear layer W_r [E, H] applied to each token,
+    logits[t, e] = sum_h x[t, h] * W_r[e, h]  (+ bias[e] when a per-expert
+    prior is given).  Returns float64 [M, E]."""
+    X = widen_bf16(x)
+    W = widen_bf16(w_router)
+    logits = X @ W.T
+    if logit_bias is not None:
+        logits = logits + np.asarray(logit_bias, dtype=np.float32).astype(np.float64)
+    return logits
+
+
+def topk_margin(logits_f32: np.ndarray, top_k: int) -> np.ndarray:
+    """Smallest gap between consecutive sorted logits that decides a token's
+    ordered top-k: min over j = 1..k of (l_(j) - l_(j+1)) (the (k+1)-th only
+    when k < E).  A token whose margin is tiny may be routed differently by
+    any implementation whose logits differ in the last bits."""
+    s = -np.sort(-np.asarray(logits_f32, dtype=np.float64), axis=1)
+    last = min(top_k + 1, s.shape[1])
+    if last < 2:
+        return np.full(s.shape[0], np.inf)
+    gaps = s[:, :last - 1] - s[:, 1:last]
+    return gaps.min(axis=1)
+
+
+def route(x: np.ndarray, w_router: np.ndarray, top_k: int, renormalize: bool,
+          logit_bias: np.ndarray | None = None) -> dict:
+    """The router steps in the page's order:
+      1. softmax over all E scores;
+      2. keep the top_k largest -> top_k expert ids and weights, slot 0 the
+         largest (exact ties go to the lower expert id);
+      3. if renormalize, rescale the kept weights to sum to 1.
+
+    Returns dict(topk_ids int32 [M, k], topk_weights float64 [M, k],
+    logits float64 [M, E], logits_f32 float32 [M, E], margin float64 [M]).
+    """
+    logits = router_logits(x, w_router, logit_bias)
+    M, E = logits.shape
+    assert 1 <= top_k <= E
+    logits_f32 = logits.astype(np.float32)
+    # 1. softmax over all experts
+    shifted = logits - logits.max(axis=1, keepdims=True)
+    ex = np.exp(shifted)
+    prob = ex / ex.sum(axis=1, keepdims=True)
+    # 2. the k largest, descending; ties -> lower id.  Softmax is strictly
+    #    increasing, so ordering the float32 logits orders the probabilities.
+    idx = np.broadcast_to(np.arange(E), (M, E))
+    order = np.lexsort((idx, -logits_f32), axis=1)
+    topk_ids = order[:, :top_k].astype(np.int32)
+    w = np.take_along_axis(prob, topk_ids.astype(np.int64), axis=1)
+    # 3. renormalize
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return dict(topk_ids=topk_ids, topk_weights=w, logits=logits,
+                logits_f32=logits_f32, margin=topk_margin(logits_f32, top_k))
+
+
+# ---------------------------------------------------------------------------
+# grouping: [MoE-vLLM] "A batch: (token, expert) pairs" (pair id p = t*k + j),
+# "Group the pairs by expert, and the GEMM shapes", and
+# "How vLLM runs the layer: two index lists and no copies", sub-section
+# "The two index lists" (moe_align_block_size)
+# ---------------------------------------------------------------------------
+
+def align(topk_ids: np.ndarray, num_experts: int, block_m: int) -> dict:
+    """The two index lists built from topk_ids.
+
+    Pair p is cell p of topk_ids read row by row (p = t*top_k + j).
+    sorted_token_ids lists the pair ids grouped by expert, experts in
+    ascending order; each group is padded with the id P = M*top_k (not a real
+    pair) up to a multiple of block_m; empty experts get no block.  Inside a
+    group the pages leave the order free; this oracle uses ascending pair id.
+    expert_ids holds the expert of every block of block_m entries.
+    expert_block_offsets[e] is the first block of expert e (length E+1, the
+    last entry is the number of blocks); expert_counts[e] = n_e.
+    """
+    flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    P = flat.size
+    E = num_experts
+    sorted_ids: list[int] = []
+    expert_ids: list[int] = []
+    offsets = [0]
+    counts = []
+    for e in range(E):
+        members = np.nonzero(flat == e)[0]          # ascending pair ids
+        n_e = members.size
+        counts.append(n_e)
+        nblk = -(-n_e // block_m)
+        sorted_ids.extend(int(p) for p in members)
+        sorted_ids.extend([P] * (nblk * block_m - n_e))
+        expert_ids.extend([e] * nblk)
+        offsets.append(offsets[-1] + nblk)
+    return dict(sorted_token_ids=np.asarray(sorted_ids, dtype=np.int32),
+                expert_ids=np.asarray(expert_ids, dtype=np.int32),
+                expert_block_offsets=np.asarray(offsets, dtype=np.int32),
+                expert_counts=np.asarray(counts, dtype=np.int32),
+                num_blocks=offsets[-1], pad_id=P)
+
+
+# ---------------------------------------------------------------------------
+# one expert: [MoE-vLLM] "One expert, and one token", sub-section
+# "An expert is a small SwiGLU MLP"
+# ---------------------------------------------------------------------------
+
+def swiglu(h: np.ndarray, I: int) -> np.ndarray:
+    """a = SiLU(h_gate) * h_up with h_gate = the first I values of h and
+    h_up = the last I; SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
+    g = h[..., :I]
+    u = h[..., I:]
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    return silu * u
+
+
+def expert_ffn(x_rows: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray,
+               return_act: bool = False):
+    """f_e on a stack of rows: h = x W13_e^T ([n, 2I]), a = SwiGLU(h),
+    y = a W2_e^T ([n, H]).  x_rows float64 [n, H]; weights bf16 bits."""
+    W13 = widen_bf16(w13_e)
+    W2 = widen_bf16(w2_e)
+    I = W2.shape[1]
+    h = x_rows @ W13.T
+    a = swiglu(h, I)
+    y = a @ W2.T
+    return (y, a) if return_act else y
+
+
+# ---------------------------------------------------------------------------
+# the layer: group by expert -> one GEMM pair per expert -> put each result
+# back into its pair slot [M, k, H] -> weighted sum over the k slots.
+# [MoE-vLLM] "Group the pairs by expert, and the GEMM shapes",
+# "Put the results back, and combine them per token".
+# ---------------------------------------------------------------------------
+
+def _pairs_by_expert(topk_ids: np.ndarray, tokens: np.ndarray):
+    """For the given tokens, yield (expert, token array, slot array)."""
+    k = topk_ids.shape[1]
+    sub = np.asarray(topk_ids)[tokens]                       # [T, k]
+    t_of = np.repeat(tokens, k)
+    j_of = np.tile(np.arange(k), tokens.size)
+    e_of = sub.reshape(-1)
+    for e in np.unique(e_of):
+        sel = np.nonzero(e_of == e)[0]
+        yield int(e), t_of[sel], j_of[sel]
+
+
+def pair_activations(x: np.ndarray, w13: np.ndarray, topk_ids: np.ndarray,
+                     tokens: np.ndarray | None = None) -> np.ndarray:
+    """GEMM 1 + SiLU-and-mul for every pair, in pair order: row p = t*k + j
+    holds a = SwiGLU(W13_{id} x_t).  Returns float64 [M*k, I] (rows of tokens
+    not asked for are left as NaN)."""
+    M, k = topk_ids.shape
+    I = w13.shape[1] // 2
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    X = widen_bf16(x)
+    act = np.full((M * k, I), np.nan)
+    for e, ts, js in _pairs_by_expert(topk_ids, tokens):
+        W13 = widen_bf16(w13[e])
+        act[ts * k + js] = swiglu(X[ts] @ W13.T, I)
+    return act
+
+
+def layer_forward(x: np.ndarray, w13: np.ndarray, w2: np.ndarray,
+                  topk_ids: np.ndarray, topk_weights: np.ndarray,
+                  tokens: np.ndarray | None = None) -> np.ndarray:
+    """y_t = sum_j w[t, j] * f_{id[t, j]}(x_t) for the requested tokens.
+
+    Steps as the pages give them: group the pairs by expert, run expert e on
+    its rows, send each output row back to its pair slot, then multiply each
+    slot by its router weight and add the top_k slots of each token.
+    Returns float64 [len(tokens), H] (all tokens when tokens is None)."""
+    M, k = topk_ids.shape
+    H = x.shape[1]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    pos = np.full(M, -1)
+    pos[tokens] = np.arange(tokens.size)
+    X = widen_bf16(x)
+    slots = np.zeros((tokens.size, k, H))
+    for e, ts, js in _pairs_by_expert(topk_ids, tokens):
+        slots[pos[ts], js] = expert_ffn(X[ts], w13[e], w2[e])
+    wts = np.asarray(topk_weights, dtype=np.float64)[tokens]
+    return np.einsum("tk,tkh->th", wts, slots)
+
+
+def combine_from_act(act_bits: np.ndarray, w2: np.ndarray,
+                     topk_ids: np.ndarray, topk_weights: np.ndarray,
+                     tokens: np.ndarray | None = None) -> np.ndarray:
+    """Second half of the layer from given activations: for each pair p,
+    y_p = W2_{id_p} a_p, then out_t = sum_j w[t, j] y_{t*k+j}.
+    act_bits: bf16 bits [M*k, I] in pair order.  Returns float64 [T, H]."""
+    M, k = topk_ids.shape
+    H = w2.shape[1]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    pos = np.full(M, -1)
+    pos[tokens] = np.arange(tokens.size)
+    A = widen_bf16(act_bits)
+    slots = np.zeros((tokens.size, k, H))
+    for e, ts, js in _pairs_by_expert(topk_ids, tokens):
+        W2 = widen_bf16(w2[e])
+        slots[pos[ts], js] = A[ts * k + js] @ W2.T
+    wts = np.asarray(topk_weights, dtype=np.float64)[tokens]
+    return np.einsum("tk,tkh->th", wts, slots)
+
+
+def forward(layer: dict, block_m: int | None = None,
+            tokens: np.ndarray | None = None) -> dict:
+    """Whole layer for a dict made by ``moe_workloads.make_layer``:
+    routing, (optionally) the index lists, and the output of the requested
+    tokens (routing is computed for those tokens only)."""
+    x = layer["x"]
+    M = x.shape[0]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    r = route(x[tokens], layer["w_router"], layer["top_k"],
+              layer["renormalize"], layer.get("logit_bias"))
+    ids = np.zeros((M, layer["top_k"]), dtype=np.int32)
+    wts = np.zeros((M, layer["top_k"]))
+    ids[tokens] = r["topk_ids"]
+    wts[tokens] = r["topk_weights"]
+    out = dict(route=r, tokens=tokens)
+    if block_m is not None and tokens.size == M:
+        out["align"] = align(ids, layer["E"], block_m)
+    out["y"] = layer_forward(x, layer["w13"], layer["w2"], ids, wts, tokens)
+    return out
