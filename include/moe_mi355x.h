@@ -1,0 +1,205 @@
+/*
+ * moe_mi355x.h -- C ABI of a one-GPU mixture-of-experts SwiGLU layer forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page "Mixture of Experts in vLLM - From First Principles to
+ * fused_moe", sections "One expert, and one token" through "How vLLM runs
+ * the layer: two index lists and no copies"):
+ *
+ *   logits = W_r x                                   router, one linear layer
+ *   p      = softmax(logits) over all E experts
+ *   ids, w = the top_k largest p (slot 0 the largest; exact ties -> lower id),
+ *            rescaled to sum to 1 when renormalize is set
+ *   pair p = t*top_k + j  for token t, slot j
+ *   index lists: pair ids sorted by expert, each expert's group padded with
+ *            the id P = M*top_k up to a multiple of block_m, one expert per
+ *            block of block_m entries
+ *   act[p] = SiLU(h_gate) * h_up,  h = W13[id] x_t,  gate = rows 0..I-1,
+ *            up = rows I..2I-1 of the stacked [2I, H] matrix
+ *   out[t] = sum_j w[t, j] * (W2[id[t, j]] act[t*top_k + j])
+ *
+ * Conventions for every call below.
+ *   - bf16 tensors are passed as raw uint16_t bit patterns.
+ *   - Every pointer is a DEVICE pointer unless marked "host".  All tensors
+ *     are dense, row-major, and 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is asynchronous on that stream: it never allocates, frees or
+ *     synchronizes, and returns as soon as its kernels are queued.
+ *   - The caller owns every buffer.  Scratch memory comes from a caller
+ *     workspace sized by moe_workspace_size(); a workspace may be reused by
+ *     later calls on the same stream, but two calls in flight at once
+ *     (different streams) need two workspaces.
+ *   - Argument errors are detected on the host before anything is launched
+ *     and return a negative moe_status; nothing is written then.  M == 0 is
+ *     valid and launches nothing.  A failed launch returns MOE_ERR_HIP.
+ *   - Device-side preconditions are the caller's: expert ids given to
+ *     moe_align and the GEMM calls must lie in [0, E), and index lists given
+ *     to the GEMM calls must be ones moe_align produced for the same
+ *     (topk_ids, E, block_m).  Breaking them is undefined behaviour.
+ *   - Supported sizes: 1 <= E <= 512; 1 <= top_k <= min(E, 32); H and I
+ *     positive multiples of 8; M*top_k < 2^24.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad flag   */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside the supported sizes   */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or too small          */
+  MOE_ERR_HIP = -4           /* a HIP launch failed                     */
+} moe_status;
+
+/* Which kernel family ran; filled by the GEMM calls and moe_forward.
+ * (host struct)  A caller can check what ran instead of inferring it from
+ * timing. */
+#define MOE_VARIANT_TILED 0   /* LDS-tiled MFMA grouped GEMM (many rows per expert) */
+#define MOE_VARIANT_STREAM 1  /* weight-streaming MFMA kernel (about one row per expert) */
+typedef struct moe_dispatch_info {
+  int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
+  int block_m;   /* rows (pairs) per block of the index lists                    */
+  int block_n;   /* output features per workgroup tile of GEMM 1 (gate + up)     */
+  int block_k;   /* K elements per pipeline step                                 */
+  int k_tail;    /* 1 if some K (H for GEMM 1, I for GEMM 2) is not a multiple of block_k */
+  int launches;  /* kernels this call queued                                     */
+} moe_dispatch_info;
+
+/* Bytes of workspace that moe_forward needs for any M <= M_max with these
+ * layer sizes (it also covers moe_route and moe_grouped_gemm_w2_combine).
+ * Returns 0 for unsupported sizes. */
+size_t moe_workspace_size(int M_max, int E, int top_k, int H, int I);
+
+/* Static text of a moe_status value. */
+const char* moe_strerror(int status);
+
+/* The block size (block_m) moe_forward uses for a batch of M tokens: the
+ * compiled tile table, keyed on the mean number of pairs per expert
+ * (M*top_k/E).  Returns 16 (weight-streaming kernels), 64 or 128 (tiled). */
+int moe_pick_block_m(int M, int E, int top_k);
+
+/*
+ * moe_route -- router logits, softmax over all experts, top-k, renormalize.
+ * Page "Mixture of Experts in vLLM ...", section "One expert, and one token",
+ * sub-section "One token uses only 8 experts"; the output format is that of
+ * section "A batch: (token, expert) pairs" (topk_ids, topk_weights [M, k]).
+ *
+ *   x            [M, H] bf16      token rows
+ *   w_router     [E, H] bf16      router weights
+ *   logit_bias   [E] fp32 or NULL added to every token's logits (a prior)
+ *   topk_ids     [M, top_k] int32 out: expert ids, slot 0 = largest
+ *   topk_weights [M, top_k] fp32  out: the kept softmax probabilities,
+ *                                 rescaled to sum 1 if renormalize != 0
+ *   logits_out   [M, E] fp32 or NULL  out: the fp32 logits (+ bias)
+ *   workspace    device scratch of ws_bytes >= moe_workspace_size(M, E,
+ *                top_k, 8, 8); may be NULL when logits_out is given.
+ * Logits accumulate bf16 x bf16 products in fp32; the top-k decision is
+ * taken on those fp32 values.
+ */
+int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+              int M, int H, int E, int top_k, int renormalize,
+              int32_t* topk_ids, float* topk_weights, float* logits_out,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_align -- the two index lists (moe_align_block_size).
+ * Page "Mixture of Experts in vLLM ...", section "How vLLM runs the layer:
+ * two index lists and no copies", sub-section "The two index lists"; pair
+ * ids as in section "A batch: (token, expert) pairs".
+ *
+ *   topk_ids             [M*top_k] int32  expert of pair p = t*top_k + j
+ *   block_m              rows per block, 1..256
+ *   sorted_token_ids     out [P + min(E,P)*(block_m-1)] int32: pair ids
+ *                        grouped by expert (ascending expert; inside a
+ *                        group ascending pair id), each group padded with
+ *                        P = M*top_k to a multiple of block_m.  Only the
+ *                        first num_blocks*block_m entries are written.
+ *   expert_ids           out [ceil(P/block_m) + min(E,P)] int32: expert of
+ *                        each block; only the first num_blocks are written.
+ *   expert_block_offsets out [E+1] int32: first block of each expert;
+ *                        entry E = num_blocks.  It stays in device memory;
+ *                        later calls read it there, so no host sync is needed.
+ *   expert_counts        out [E] int32 (pairs per expert) or NULL.
+ * The result is deterministic (the same bits on every run).
+ */
+int moe_align(const int32_t* topk_ids, int M, int top_k, int E, int block_m,
+              int32_t* sorted_token_ids, int32_t* expert_ids,
+              int32_t* expert_block_offsets, int32_t* expert_counts, void* stream);
+
+/*
+ * moe_grouped_gemm_w13_act -- grouped GEMM 1 with SiLU(gate)*up fused.
+ * Page "Mixture of Experts in vLLM ...", sub-sections "One GEMM 1 program,
+ * step by step" (block -> expert, pad mask, input row p // top_k, output row
+ * p) and "The rest of the layer stays in pair order" (SiLU and multiply row
+ * by row).  The [M*top_k, 2I] GEMM 1 output never exists in memory.
+ *
+ *   x      [M, H] bf16;  w13 [E, 2I, H] bf16 (gate rows first)
+ *   index lists from moe_align with the same block_m (16, 64 or 128;
+ *   16 selects the weight-streaming kernel, 64/128 the tiled kernel)
+ *   act    out [M*top_k, I] bf16 in pair order (row p = t*top_k + j)
+ *   info   host, optional: which kernel ran
+ * Accumulation is fp32; act is rounded to bf16 once.
+ */
+int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
+                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                             const int32_t* expert_block_offsets,
+                             int M, int top_k, int E, int H, int I, int block_m,
+                             uint16_t* act, moe_dispatch_info* info, void* stream);
+
+/*
+ * moe_grouped_gemm_w2_combine -- grouped GEMM 2 with the weighted top-k
+ * combine fused.  Page "Mixture of Experts in vLLM ...", sections "Put the
+ * results back, and combine them per token" and "The rest of the layer
+ * stays in pair order" (GEMM 2 reads row p, multiplies by topk_weights[p];
+ * the per-token sum).  The [M*top_k, H] GEMM 2 output never exists.
+ *
+ *   act          [M*top_k, I] bf16 in pair order
+ *   w2           [E, H, I] bf16
+ *   topk_weights [M*top_k] fp32
+ *   out          out [M, H] bf16 in token order
+ *   workspace    scratch for the fp32 per-token sums and arrival counters,
+ *                ws_bytes >= moe_workspace_size(M, E, top_k, H, I)
+ * Each output row is summed in fp32 (in arrival order, so the last bit of
+ * the bf16 result may differ between runs) and rounded to bf16 once.
+ */
+int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
+                                const float* topk_weights,
+                                const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                const int32_t* expert_block_offsets,
+                                int M, int top_k, int E, int H, int I, int block_m,
+                                uint16_t* out, void* workspace, size_t ws_bytes,
+                                moe_dispatch_info* info, void* stream);
+
+/*
+ * moe_forward -- the whole layer: route -> align -> GEMM 1 + act -> GEMM 2 +
+ * combine, all queued on `stream` with no host synchronization.  Every
+ * intermediate lives in the caller's workspace, allocated once and reused
+ * across layers (page "MoE Execution Path Analysis", "Memory allocation per
+ * step" and "What we can actually change"); block_m comes from
+ * moe_pick_block_m (the same page's per-batch-size BLOCK_SIZE_M choice).
+ *
+ *   x [M, H], w_router [E, H], w13 [E, 2I, H], w2 [E, H, I]: bf16
+ *   logit_bias       [E] fp32 or NULL
+ *   out              out [M, H] bf16
+ *   topk_ids_out     out [M, top_k] int32 or NULL
+ *   topk_weights_out out [M, top_k] fp32 or NULL
+ *   workspace        ws_bytes >= moe_workspace_size(M, E, top_k, H, I)
+ *   info             host, optional
+ */
+int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                const uint16_t* w13, const uint16_t* w2,
+                int M, int E, int top_k, int H, int I, int renormalize,
+                uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
+                void* workspace, size_t ws_bytes, moe_dispatch_info* info, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,295 @@
+"""Python binding of the MI355X MoE layer-forward library (libmoe_mi355x.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/moe_mi355x.h``.  torch supplies device
+memory and the current stream; nothing here computes any part of the layer,
+and there is no CPU fallback -- if the library is missing, importing the
+binding works but every call raises.
+
+Function names match the C ABI: moe_route, moe_align,
+moe_grouped_gemm_w13_act, moe_grouped_gemm_w2_combine, moe_forward, plus
+moe_workspace_size, moe_pick_block_m and moe_strerror.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
+
+MOE_VARIANT_TILED = 0
+MOE_VARIANT_STREAM = 1
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size_t = ctypes.c_size_t
+
+
+class MoeError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} failed: {moe_strerror(status)} (status {status})")
+        self.status = status
+
+
+class DispatchInfo(ctypes.Structure):
+    _fields_ = [("variant", _c_int), ("block_m", _c_int), ("block_n", _c_int),
+                ("block_k", _c_int), ("k_tail", _c_int), ("launches", _c_int)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_SIGNATURES = {
+    "moe_workspace_size": (_c_size_t, [_c_int] * 5),
+    "moe_strerror": (ctypes.c_char_p, [_c_int]),
+    "moe_pick_block_m": (_c_int, [_c_int] * 3),
+    "moe_route": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                           _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                           _c_void_p]),
+    "moe_align": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                           _c_void_p, _c_void_p, _c_void_p]),
+    "moe_grouped_gemm_w13_act": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
+                                 [_c_void_p, ctypes.POINTER(DispatchInfo), _c_void_p]),
+    "moe_grouped_gemm_w2_combine": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 +
+                                    [_c_void_p, _c_void_p, _c_size_t,
+                                     ctypes.POINTER(DispatchInfo), _c_void_p]),
+    "moe_forward": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
+                    [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                     ctypes.POINTER(DispatchInfo), _c_void_p]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmoe_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -c "
+                "'import __graft_entry__ as g; g.build()'); there is no fallback path")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def moe_workspace_size(M_max: int, E: int, top_k: int, H: int, I: int) -> int:
+    return int(library().moe_workspace_size(M_max, E, top_k, H, I))
+
+
+def moe_strerror(status: int) -> str:
+    return library().moe_strerror(status).decode()
+
+
+def moe_pick_block_m(M: int, E: int, top_k: int) -> int:
+    return int(library().moe_pick_block_m(M, E, top_k))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtypes, shape=None):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.data_ptr() % 16 != 0:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    del torch
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _raise(call: str, st: int):
+    if st != 0:
+        raise MoeError(call, st)
+
+
+def workspace(M_max: int, E: int, top_k: int, H: int, I: int, device=None):
+    """Allocate a workspace tensor (uint8) large enough for every call with
+    M <= M_max and these layer sizes."""
+    torch = _torch()
+    n = moe_workspace_size(M_max, E, top_k, H, I)
+    if n == 0:
+        raise MoeError("moe_workspace_size", -2)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_route(x, w_router, top_k: int, renormalize: bool = True, logit_bias=None,
+              topk_ids=None, topk_weights=None, logits_out=None, ws=None, stream=None):
+    torch = _torch()
+    M, H = x.shape
+    E = w_router.shape[0]
+    _check(x, "x", _bf16_types())
+    _check(w_router, "w_router", _bf16_types(), (E, H))
+    if logit_bias is not None:
+        _check(logit_bias, "logit_bias", (torch.float32,), (E,))
+    if topk_ids is None:
+        topk_ids = torch.empty((M, top_k), dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((M, top_k), dtype=torch.float32, device=x.device)
+    _check(topk_ids, "topk_ids", (torch.int32,), (M, top_k))
+    _check(topk_weights, "topk_weights", (torch.float32,), (M, top_k))
+    if logits_out is not None:
+        _check(logits_out, "logits_out", (torch.float32,), (M, E))
+    elif ws is None:
+        ws = torch.empty(max(M * E * 4, 16), dtype=torch.uint8, device=x.device)
+    st = library().moe_route(_ptr(x), _ptr(w_router), _ptr(logit_bias), M, H, E, top_k,
+                             int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_weights),
+                             _ptr(logits_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream))
+    _raise("moe_route", st)
+    return topk_ids, topk_weights
+
+
+def align_capacity(P: int, E: int, block_m: int) -> tuple:
+    """(sorted_token_ids length, expert_ids length) that moe_align needs."""
+    nz = min(E, P)
+    return P + nz * (block_m - 1), -(-P // block_m) + nz
+
+
+def moe_align(topk_ids, E: int, block_m: int, sorted_token_ids=None, expert_ids=None,
+              expert_block_offsets=None, expert_counts=None, stream=None):
+    torch = _torch()
+    M, top_k = topk_ids.shape
+    _check(topk_ids, "topk_ids", (torch.int32,))
+    P = M * top_k
+    cap, nbl = align_capacity(P, E, block_m)
+    dev = topk_ids.device
+    if sorted_token_ids is None:
+        sorted_token_ids = torch.empty(max(cap, 4), dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(max(nbl, 4), dtype=torch.int32, device=dev)
+    if expert_block_offsets is None:
+        expert_block_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if expert_counts is None:
+        expert_counts = torch.empty(E, dtype=torch.int32, device=dev)
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (expert_block_offsets, "expert_block_offsets"),
+                 (expert_counts, "expert_counts")):
+        _check(t, n, (torch.int32,))
+    if sorted_token_ids.numel() < cap or expert_ids.numel() < nbl or \
+            expert_block_offsets.numel() < E + 1 or expert_counts.numel() < E:
+        raise ValueError("moe_align output buffers are too small")
+    st = library().moe_align(_ptr(topk_ids), M, top_k, E, block_m, _ptr(sorted_token_ids),
+                             _ptr(expert_ids), _ptr(expert_block_offsets),
+                             _ptr(expert_counts), _stream(stream))
+    _raise("moe_align", st)
+    return sorted_token_ids, expert_ids, expert_block_offsets, expert_counts
+
+
+def moe_grouped_gemm_w13_act(x, w13, sorted_token_ids, expert_ids, expert_block_offsets,
+                             top_k: int, block_m: int, act=None, stream=None):
+    torch = _torch()
+    M, H = x.shape
+    E, two_i, H2 = w13.shape
+    I = two_i // 2
+    _check(x, "x", _bf16_types())
+    _check(w13, "w13", _bf16_types(), (E, 2 * I, H))
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (expert_block_offsets, "expert_block_offsets")):
+        _check(t, n, (torch.int32,))
+    if act is None:
+        act = torch.empty((M * top_k, I), dtype=torch.bfloat16, device=x.device)
+    _check(act, "act", _bf16_types(), (M * top_k, I))
+    info = DispatchInfo()
+    st = library().moe_grouped_gemm_w13_act(
+        _ptr(x), _ptr(w13), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(expert_block_offsets), M, top_k, E, H, I, block_m, _ptr(act),
+        ctypes.byref(info), _stream(stream))
+    _raise("moe_grouped_gemm_w13_act", st)
+    return act, info.as_dict()
+
+
+def moe_grouped_gemm_w2_combine(act, w2, topk_weights, sorted_token_ids, expert_ids,
+                                expert_block_offsets, M: int, top_k: int, block_m: int,
+                                out=None, ws=None, stream=None):
+    torch = _torch()
+    E, H, I = w2.shape
+    _check(act, "act", _bf16_types(), (M * top_k, I))
+    _check(w2, "w2", _bf16_types())
+    _check(topk_weights, "topk_weights", (torch.float32,))
+    if topk_weights.numel() != M * top_k:
+        raise ValueError("topk_weights must hold M*top_k values")
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (expert_block_offsets, "expert_block_offsets")):
+        _check(t, n, (torch.int32,))
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=act.device)
+    _check(out, "out", _bf16_types(), (M, H))
+    if ws is None:
+        ws = workspace(M, E, top_k, H, I, act.device)
+    info = DispatchInfo()
+    st = library().moe_grouped_gemm_w2_combine(
+        _ptr(act), _ptr(w2), _ptr(topk_weights), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(expert_block_offsets), M, top_k, E, H, I, block_m, _ptr(out), _ptr(ws),
+        ws.numel(), ctypes.byref(info), _stream(stream))
+    _raise("moe_grouped_gemm_w2_combine", st)
+    return out, info.as_dict()
+
+
+def moe_forward(x, w_router, w13, w2, top_k: int, renormalize: bool = True,
+                logit_bias=None, out=None, topk_ids_out=None, topk_weights_out=None,
+                ws=None, stream=None):
+    """The whole layer.  Returns (out [M, H] bf16, dispatch info dict)."""
+    torch = _torch()
+    M, H = x.shape
+    E, two_i, _ = w13.shape
+    I = two_i // 2
+    _check(x, "x", _bf16_types())
+    _check(w_router, "w_router", _bf16_types(), (E, H))
+    _check(w13, "w13", _bf16_types(), (E, 2 * I, H))
+    _check(w2, "w2", _bf16_types(), (E, H, I))
+    if logit_bias is not None:
+        _check(logit_bias, "logit_bias", (torch.float32,), (E,))
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", _bf16_types(), (M, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", (torch.int32,), (M, top_k))
+    if topk_weights_out is not None:
+        _check(topk_weights_out, "topk_weights_out", (torch.float32,), (M, top_k))
+    if ws is None:
+        ws = workspace(M, E, top_k, H, I, x.device)
+    info = DispatchInfo()
+    st = library().moe_forward(
+        _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w13), _ptr(w2), M, E, top_k, H, I,
+        int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
+        _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
+    _raise("moe_forward", st)
+    return out, info.as_dict()

@@ -1,0 +1,280 @@
+// C ABI of the MoE layer forward: argument checks, workspace carve-up,
+// kernel choice and launches.  Declarations and the contract of every call
+// are in include/moe_mi355x.h.
+#include <algorithm>
+
+#include "moe_common.h"
+#include "moe_mi355x.h"
+
+using namespace moe_host;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr long long kMaxPairs = 1LL << 24;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+long long max_blocks(long long P, int E, int B) {
+  return (P + B - 1) / B + std::min<long long>(E, P);
+}
+long long sorted_capacity(long long P, int E, int B) {
+  return P + std::min<long long>(E, P) * (B - 1);
+}
+
+// Workspace regions of moe_forward for one (M, E, top_k, H, I, block_m).
+// The fp32 per-token sums and the arrival counters are adjacent so that one
+// pass clears both.
+struct Layout {
+  size_t ids, wts, logits, sorted, eids, boff, counts, act, acc, cnt, total;
+  size_t zero_words;  // 4-byte words of acc + cnt
+};
+
+Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
+  const long long P = (long long)M * top_k;
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.acc = take(0);
+  const size_t acc_bytes = (size_t)M * H * 4;
+  const size_t cnt_bytes = (size_t)M * ((H + kCounterCols - 1) / kCounterCols) * 4;
+  L.cnt = L.acc + acc_bytes;
+  take(acc_bytes + cnt_bytes);
+  L.zero_words = (acc_bytes + cnt_bytes) / 4;
+  L.ids = take((size_t)P * 4);
+  L.wts = take((size_t)P * 4);
+  L.logits = take((size_t)M * E * 4);
+  L.sorted = take((size_t)sorted_capacity(P, E, B) * 4);
+  L.eids = take((size_t)max_blocks(P, E, B) * 4);
+  L.boff = take((size_t)(E + 1) * 4);
+  L.counts = take((size_t)E * 4);
+  L.act = take((size_t)P * I * 2);
+  L.total = off;
+  return L;
+}
+
+int check_sizes(int M, int E, int top_k, int H, int I) {
+  if (M < 0 || E <= 0 || top_k <= 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (top_k > E) return MOE_ERR_INVALID_ARG;
+  if (E > 512 || top_k > 32) return MOE_ERR_UNSUPPORTED;
+  if (H % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long long)M * top_k >= kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool gemm_block_ok(int B) { return B == 16 || B == 64 || B == 128; }
+
+void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches) {
+  if (info == nullptr) return;
+  const bool stream = B == 16;
+  info->variant = stream ? MOE_VARIANT_STREAM : MOE_VARIANT_TILED;
+  info->block_m = B;
+  info->block_n = stream ? kStreamG1Features : kTiledG1Features;
+  info->block_k = stream ? kStreamBK : kTiledBK;
+  info->k_tail = (H % info->block_k != 0 || I % info->block_k != 0) ? 1 : 0;
+  info->launches = launches;
+}
+
+#define MOE_TRY_HIP(expr)                            \
+  do {                                               \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;    \
+  } while (0)
+
+GemmArgs gemm_args(int M, int top_k, int E, int H, int I, int B) {
+  GemmArgs g{};
+  g.M = M;
+  g.top_k = top_k;
+  g.E = E;
+  g.H = H;
+  g.I = I;
+  g.block_m = B;
+  g.max_blocks = (int)max_blocks((long long)M * top_k, E, B);
+  return g;
+}
+
+int run_gemm1(GemmArgs g, hipStream_t s) {
+  MOE_TRY_HIP(g.block_m == 16 ? launch_gemm1_stream(g, s) : launch_gemm1_tiled(g, s));
+  return MOE_OK;
+}
+
+int run_gemm2(GemmArgs g, hipStream_t s) {
+  MOE_TRY_HIP(g.block_m == 16 ? launch_gemm2_stream(g, s) : launch_gemm2_tiled(g, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(int M_max, int E, int top_k, int H, int I) {
+  if (check_sizes(M_max, E, top_k, H, I) != MOE_OK) return 0;
+  size_t best = 0;
+  for (int B : {16, 64, 128})
+    best = std::max(best, forward_layout(M_max, E, top_k, H, I, B).total);
+  return std::max<size_t>(best, kAlign);
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or option";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_pick_block_m(int M, int E, int top_k) {
+  if (E <= 0) return 16;
+  const double per_expert = (double)M * top_k / E;
+  if (per_expert <= 8.0) return 16;
+  if (per_expert <= 48.0) return 64;
+  return 128;
+}
+
+int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bias, int M,
+              int H, int E, int top_k, int renormalize, int32_t* topk_ids,
+              float* topk_weights, float* logits_out, void* workspace, size_t ws_bytes,
+              void* stream) {
+  int st = check_sizes(M, E, top_k, H, 8);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+  float* logits = logits_out;
+  if (logits == nullptr) {
+    if (workspace == nullptr || ws_bytes < (size_t)M * E * 4) return MOE_ERR_WORKSPACE;
+    logits = static_cast<float*>(workspace);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteArgs a{x, w_router, logit_bias, M, H, E, top_k, renormalize, logits, topk_ids,
+              topk_weights, nullptr, 0};
+  MOE_TRY_HIP(launch_route_logits(a, s));
+  MOE_TRY_HIP(launch_route_topk(a, s));
+  return MOE_OK;
+}
+
+int moe_align(const int32_t* topk_ids, int M, int top_k, int E, int block_m,
+              int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* expert_block_offsets,
+              int32_t* expert_counts, void* stream) {
+  int st = check_sizes(M, E, top_k, 8, 8);
+  if (st != MOE_OK) return st;
+  if (block_m < 1 || block_m > 256) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!topk_ids || !sorted_token_ids || !expert_ids || !expert_block_offsets)
+    return MOE_ERR_INVALID_ARG;
+  AlignArgs a{topk_ids, M * top_k, E, block_m, sorted_token_ids, expert_ids,
+              expert_block_offsets, expert_counts};
+  MOE_TRY_HIP(launch_align(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
+                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                             const int32_t* expert_block_offsets, int M, int top_k, int E,
+                             int H, int I, int block_m, uint16_t* act,
+                             moe_dispatch_info* info, void* stream) {
+  int st = check_sizes(M, E, top_k, H, I);
+  if (st != MOE_OK) return st;
+  if (!gemm_block_ok(block_m)) return MOE_ERR_UNSUPPORTED;
+  fill_info(info, block_m, H, I, M == 0 ? 0 : 1);
+  if (M == 0) return MOE_OK;
+  if (!x || !w13 || !sorted_token_ids || !expert_ids || !expert_block_offsets || !act)
+    return MOE_ERR_INVALID_ARG;
+  GemmArgs g = gemm_args(M, top_k, E, H, I, block_m);
+  g.a_src = x;
+  g.w = w13;
+  g.sorted_token_ids = sorted_token_ids;
+  g.expert_ids = expert_ids;
+  g.expert_block_offsets = expert_block_offsets;
+  g.out = act;
+  return run_gemm1(g, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
+                                const float* topk_weights, const int32_t* sorted_token_ids,
+                                const int32_t* expert_ids, const int32_t* expert_block_offsets,
+                                int M, int top_k, int E, int H, int I, int block_m,
+                                uint16_t* out, void* workspace, size_t ws_bytes,
+                                moe_dispatch_info* info, void* stream) {
+  int st = check_sizes(M, E, top_k, H, I);
+  if (st != MOE_OK) return st;
+  if (!gemm_block_ok(block_m)) return MOE_ERR_UNSUPPORTED;
+  fill_info(info, block_m, H, I, M == 0 ? 0 : 2);
+  if (M == 0) return MOE_OK;
+  if (!act || !w2 || !topk_weights || !sorted_token_ids || !expert_ids ||
+      !expert_block_offsets || !out)
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = forward_layout(M, E, top_k, H, I, block_m);
+  const size_t need = L.zero_words * 4;
+  if (workspace == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  MOE_TRY_HIP(launch_fill_zero(reinterpret_cast<float*>(ws + L.acc), L.zero_words, s));
+  GemmArgs g = gemm_args(M, top_k, E, H, I, block_m);
+  g.a_src = act;
+  g.w = w2;
+  g.topk_weights = topk_weights;
+  g.sorted_token_ids = sorted_token_ids;
+  g.expert_ids = expert_ids;
+  g.expert_block_offsets = expert_block_offsets;
+  g.out = out;
+  g.acc = reinterpret_cast<float*>(ws + L.acc);
+  g.counters = reinterpret_cast<int32_t*>(ws + L.cnt);
+  return run_gemm2(g, s);
+}
+
+int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                const uint16_t* w13, const uint16_t* w2, int M, int E, int top_k, int H, int I,
+                int renormalize, uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
+                void* workspace, size_t ws_bytes, moe_dispatch_info* info, void* stream) {
+  int st = check_sizes(M, E, top_k, H, I);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  const int B = moe_pick_block_m(M, E, top_k);
+  fill_info(info, B, H, I, M == 0 ? 0 : 5);
+  if (M == 0) return MOE_OK;
+  if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+  const Layout L = forward_layout(M, E, top_k, H, I, B);
+  if (workspace == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(ws + L.wts);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(ws + L.eids);
+  int32_t* boff = reinterpret_cast<int32_t*>(ws + L.boff);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+
+  RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
+               reinterpret_cast<float*>(ws + L.logits), ids, wts,
+               reinterpret_cast<float*>(ws + L.acc), L.zero_words};
+  MOE_TRY_HIP(launch_route_logits(ra, s));
+  MOE_TRY_HIP(launch_route_topk(ra, s));
+  AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
+               reinterpret_cast<int32_t*>(ws + L.counts)};
+  MOE_TRY_HIP(launch_align(aa, s));
+  GemmArgs g = gemm_args(M, top_k, E, H, I, B);
+  g.sorted_token_ids = sorted;
+  g.expert_ids = eids;
+  g.expert_block_offsets = boff;
+  g.a_src = x;
+  g.w = w13;
+  g.out = act;
+  st = run_gemm1(g, s);
+  if (st != MOE_OK) return st;
+  g.a_src = act;
+  g.w = w2;
+  g.topk_weights = wts;
+  g.out = out;
+  g.acc = reinterpret_cast<float*>(ws + L.acc);
+  g.counters = reinterpret_cast<int32_t*>(ws + L.cnt);
+  return run_gemm2(g, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and its host-side logic (workspace sizes, tile table, argument
+checks) behaves as documented.  No call here reaches the GPU: every call
+either computes on the host or is rejected before any launch."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def _moe():
+    import mixture_experts_ffn_renorm_amd as moe
+    return moe
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    moe = _moe()
+    lib = moe.library()
+    names = declared_functions()
+    assert set(names) >= {"moe_route", "moe_align", "moe_grouped_gemm_w13_act",
+                          "moe_grouped_gemm_w2_combine", "moe_forward", "moe_workspace_size",
+                          "moe_strerror", "moe_pick_block_m"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    # binding signatures cover exactly the declared calls
+    assert set(moe._SIGNATURES) == set(names)
+
+
+def test_strerror():
+    moe = _moe()
+    assert moe.moe_strerror(0) == "ok"
+    assert "workspace" in moe.moe_strerror(-3)
+    assert moe.moe_strerror(12345) == "unknown status"
+
+
+def test_tile_table():
+    moe = _moe()
+    assert moe.moe_pick_block_m(1, 128, 8) == 16
+    assert moe.moe_pick_block_m(64, 128, 8) == 16
+    assert moe.moe_pick_block_m(16, 60, 4) == 16
+    assert moe.moe_pick_block_m(512, 60, 4) == 64
+    assert moe.moe_pick_block_m(2048, 60, 4) == 128
+    assert moe.moe_pick_block_m(4096, 128, 8) == 128
+    assert moe.moe_pick_block_m(8192, 256, 8) == 128
+    assert moe.moe_pick_block_m(8, 256, 8) == 16
+
+
+def test_workspace_size_monotone_and_bounded():
+    moe = _moe()
+    prev = 0
+    for M in (1, 2, 8, 64, 512, 4096, 8192):
+        n = moe.moe_workspace_size(M, 256, 8, 2048, 512)
+        assert n >= prev
+        prev = n
+    # act [P, I] bf16 + fp32 sums [M, H] dominate: about 135 MB at M = 8192
+    n = moe.moe_workspace_size(8192, 256, 8, 2048, 512)
+    P = 8192 * 8
+    assert P * 512 * 2 + 8192 * 2048 * 4 <= n <= 1.2 * (P * 512 * 2 + 8192 * 2048 * 4) + (8 << 20)
+    assert moe.moe_workspace_size(1, 600, 8, 2048, 512) == 0     # E > 512
+    assert moe.moe_workspace_size(1, 128, 8, 2044, 512) == 0     # H % 8 != 0
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NULL, NULL, NULL, NULL, NULL, -1, 128, 8, 2048, 768, 1), -1),     # M < 0
+    ((NULL, NULL, NULL, NULL, NULL, 4, 128, 0, 2048, 768, 1), -1),      # top_k = 0
+    ((NULL, NULL, NULL, NULL, NULL, 4, 4, 8, 2048, 768, 1), -1),        # top_k > E
+    ((NULL, NULL, NULL, NULL, NULL, 4, 600, 8, 2048, 768, 1), -2),      # E > 512
+    ((NULL, NULL, NULL, NULL, NULL, 4, 128, 40, 2048, 768, 1), -2),     # top_k > 32
+    ((NULL, NULL, NULL, NULL, NULL, 4, 128, 8, 2044, 768, 1), -2),      # H % 8
+    ((NULL, NULL, NULL, NULL, NULL, 4, 128, 8, 2048, 770, 1), -2),      # I % 8
+    ((NULL, NULL, NULL, NULL, NULL, 4, 128, 8, 2048, 768, 2), -1),      # renormalize flag
+    ((NULL, NULL, NULL, NULL, NULL, 4, 128, 8, 2048, 768, 1), -1),      # null pointers
+    ((NULL, NULL, NULL, NULL, NULL, 0, 128, 8, 2048, 768, 1), 0),       # M = 0: no launch
+])
+def test_forward_argument_checks(args, status):
+    lib = _moe().library()
+    st = lib.moe_forward(*args, NULL, NULL, NULL, NULL, 0, NULL, NULL)
+    assert st == status
+
+
+def test_forward_workspace_too_small():
+    lib = _moe().library()
+    fake = ctypes.c_void_p(0x10000)      # never dereferenced: the size check fails first
+    st = lib.moe_forward(fake, fake, NULL, fake, fake, 4, 128, 8, 2048, 768, 1, fake, NULL,
+                         NULL, fake, 1024, NULL, NULL)
+    assert st == -3
+    st = lib.moe_forward(fake, fake, NULL, fake, fake, 4, 128, 8, 2048, 768, 1, fake, NULL,
+                         NULL, NULL, 1 << 30, NULL, NULL)
+    assert st == -3
+
+
+def test_other_calls_argument_checks():
+    moe = _moe()
+    lib = moe.library()
+    fake = ctypes.c_void_p(0x10000)
+    info = moe.DispatchInfo()
+    # align: block_m out of range, null outputs, M = 0
+    assert lib.moe_align(fake, 4, 2, 8, 0, fake, fake, fake, NULL, NULL) == -2
+    assert lib.moe_align(fake, 4, 2, 8, 300, fake, fake, fake, NULL, NULL) == -2
+    assert lib.moe_align(fake, 4, 2, 8, 16, NULL, fake, fake, NULL, NULL) == -1
+    assert lib.moe_align(fake, 0, 2, 8, 16, NULL, NULL, NULL, NULL, NULL) == 0
+    # GEMMs: block_m must be 16, 64 or 128
+    assert lib.moe_grouped_gemm_w13_act(fake, fake, fake, fake, fake, 4, 2, 8, 64, 32, 32,
+                                        fake, ctypes.byref(info), NULL) == -2
+    assert lib.moe_grouped_gemm_w13_act(fake, fake, fake, fake, fake, 0, 2, 8, 64, 32, 16,
+                                        fake, ctypes.byref(info), NULL) == 0
+    assert info.variant == moe.MOE_VARIANT_STREAM and info.block_m == 16 and info.launches == 0
+    assert lib.moe_grouped_gemm_w2_combine(fake, fake, fake, fake, fake, fake, 4, 2, 8, 64, 32,
+                                           64, fake, fake, 16, ctypes.byref(info), NULL) == -3
+    assert lib.moe_grouped_gemm_w2_combine(fake, fake, fake, fake, fake, fake, 0, 2, 8, 64, 32,
+                                           64, fake, NULL, 0, ctypes.byref(info), NULL) == 0
+    assert info.variant == moe.MOE_VARIANT_TILED and info.block_k == 64
+    # route: needs a logits buffer or a workspace
+    assert lib.moe_route(fake, fake, NULL, 4, 64, 8, 2, 1, fake, fake, NULL, NULL, 0, NULL) == -3
+    assert lib.moe_route(fake, fake, NULL, 4, 64, 8, 9, 1, fake, fake, NULL, NULL, 0, NULL) == -1
+
+
+def test_dispatch_info_forward_readout():
+    moe = _moe()
+    lib = moe.library()
+    info = moe.DispatchInfo()
+    assert lib.moe_forward(NULL, NULL, NULL, NULL, NULL, 0, 60, 4, 2048, 1408, 1, NULL, NULL,
+                           NULL, NULL, 0, ctypes.byref(info), NULL) == 0
+    assert info.variant == moe.MOE_VARIANT_STREAM and info.k_tail == 1

@@ -1,0 +1,155 @@
+"""GPU parity of the whole layer (moe_forward) against the CPU oracle on
+every workload shape, plus the layer's special cases and robustness checks.
+
+Routing ids are compared bit-exactly on tokens whose top-k logit margin
+exceeds 1e-4; outputs are compared on those tokens with the max-abs and
+mean-relative criteria.  At the large batch sizes the oracle checks a seeded
+sample of tokens (it computes them one expert group at a time)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import moe_workloads as wl
+from oracle import moe_oracle as mo
+from tests import helpers as h
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import mixture_experts_ffn_renorm_amd as moe
+    return moe
+
+
+def run_forward(lay: dict, ws=None, out=None):
+    import torch
+    moe = _moe()
+    d = h.layer_to_device(lay)
+    M, k = lay["M"], lay["top_k"]
+    ids = torch.full((M, k), -1, dtype=torch.int32, device="cuda")
+    wts = torch.full((M, k), -1.0, dtype=torch.float32, device="cuda")
+    out, info = moe.moe_forward(d["x"], d["w_router"], d["w13"], d["w2"], k,
+                                lay["renormalize"], logit_bias=d["logit_bias"], out=out,
+                                topk_ids_out=ids, topk_weights_out=wts, ws=ws)
+    torch.cuda.synchronize()
+    return out, ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64), info
+
+
+def check_forward(lay: dict, n_tokens: int = 256, seed: int = 0, **kw):
+    out, ids, wts, info = run_forward(lay, **kw)
+    M = lay["M"]
+    toks = h.sample_tokens(M, n_tokens, seed)
+    ref = mo.forward(lay, tokens=toks)
+    r = ref["route"]
+    ok = r["margin"] > h.MARGIN
+    assert ok.mean() >= 0.9
+    assert np.array_equal(ids[toks][ok], r["topk_ids"][ok])
+    assert np.abs(wts[toks][ok] - r["topk_weights"][ok]).max() <= h.WEIGHT_TOL
+    y = h.host_bf16_to_f64(out)[toks]
+    h.assert_close_outputs(y[ok], ref["y"][ok])
+    return info, out
+
+
+FORWARD_CASES = [("toy", 3)] + [("qwen3_decode", m) for m in (1, 2, 8, 16, 64)] + \
+    [("qwen3_prefill", 4096)] + [("qwen15", m) for m in (1, 16, 512, 2048)] + \
+    [("wide256", m) for m in (1, 8, 8192)]
+
+
+@pytest.mark.parametrize("name,M", FORWARD_CASES)
+def test_forward_workloads(name, M):
+    moe = _moe()
+    lay = wl.make_layer(name, M)
+    info, _ = check_forward(lay)
+    B = moe.moe_pick_block_m(M, lay["E"], lay["top_k"])
+    assert info["block_m"] == B
+    assert info["variant"] == (moe.MOE_VARIANT_STREAM if B == 16 else moe.MOE_VARIANT_TILED)
+    if name in ("qwen3_decode",) or (name, M) in (("wide256", 1), ("wide256", 8)):
+        assert info["variant"] == moe.MOE_VARIANT_STREAM
+    if (name, M) in (("qwen3_prefill", 4096), ("wide256", 8192)):
+        assert info["variant"] == moe.MOE_VARIANT_TILED
+    bk = info["block_k"]
+    assert info["k_tail"] == int(lay["H"] % bk != 0 or lay["I"] % bk != 0)
+    if name == "qwen15" and B == 16:
+        assert info["k_tail"] == 1       # I = 1408 is not a multiple of 256
+
+
+def test_forward_zipf_prefill_has_empty_experts():
+    """The skewed prefill layer routes no pair to some experts and very many
+    to a few; the layer output still matches."""
+    lay = wl.make_layer("qwen3_prefill", 4096)
+    _, ids, _, _ = run_forward(lay)
+    counts = np.bincount(ids.reshape(-1), minlength=lay["E"])
+    assert (counts == 0).sum() >= 1 and counts.max() > 2048
+
+
+def test_forward_dense_single_expert():
+    """E = 1, top_k = 1: a dense SwiGLU FFN."""
+    lay = wl.make_layer("toy", 33, E=1, top_k=1, H=128, I=64, seed=9)
+    check_forward(lay)
+
+
+def test_forward_identical_experts():
+    lay = wl.make_layer("toy", 40, E=8, top_k=3, H=128, I=64, seed=10)
+    lay["w13"][:] = lay["w13"][0]
+    lay["w2"][:] = lay["w2"][0]
+    out, _, _, _ = run_forward(lay)
+    f = mo.expert_ffn(mo.widen_bf16(lay["x"]), lay["w13"][0], lay["w2"][0])
+    h.assert_close_outputs(h.host_bf16_to_f64(out), f)
+
+
+def test_forward_renormalize_off_and_k_equals_E():
+    lay = wl.make_layer("toy", 3)
+    lay["renormalize"] = False
+    check_forward(lay)
+    lay = wl.make_layer("toy", 5, top_k=4, seed=12)
+    check_forward(lay)
+
+
+def test_forward_zero_tokens():
+    import torch
+    moe = _moe()
+    lay = wl.make_layer("toy", 3)
+    d = h.layer_to_device(lay)
+    x0 = d["x"][:0]
+    out, info = moe.moe_forward(x0, d["w_router"], d["w13"], d["w2"], 2, True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64) and info["launches"] == 0
+
+
+def test_forward_poisoned_workspace_and_guard_bands():
+    """Workspace filled with NaN bytes before the call; output rows written
+    through a view with canary rows on both sides."""
+    import torch
+    moe = _moe()
+    lay = wl.make_layer("qwen3_decode", 16)
+    M, H = lay["M"], lay["H"]
+    ws = moe.workspace(M, lay["E"], lay["top_k"], H, lay["I"])
+    ws.fill_(0xFF)
+    buf = torch.full((M + 2, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    check_forward(lay, ws=ws, out=buf[1:M + 1])
+    assert torch.all(buf[0] == 7.0) and torch.all(buf[M + 1] == 7.0)
+    # the same workspace again, now holding the last call's contents
+    check_forward(lay, ws=ws, out=buf[1:M + 1])
+
+
+def test_forward_workspace_reuse_across_sizes():
+    """One workspace sized for the largest batch serves smaller ones."""
+    moe = _moe()
+    big = wl.make_layer("qwen15", 512)
+    ws = moe.workspace(512, big["E"], big["top_k"], big["H"], big["I"])
+    check_forward(big, ws=ws)
+    small = wl.make_layer("qwen15", 16)
+    check_forward(small, ws=ws)
+
+
+def test_forward_repeatable():
+    """Routing is bitwise repeatable; outputs agree to the bf16 rounding of
+    fp32 sums added in a different order."""
+    lay = wl.make_layer("wide256", 8)
+    o1, i1, w1, _ = run_forward(lay)
+    o2, i2, w2, _ = run_forward(lay)
+    assert np.array_equal(i1, i2) and np.array_equal(w1, w2)
+    a, b = h.host_bf16_to_f64(o1), h.host_bf16_to_f64(o2)
+    assert np.abs(a - b).max() <= 2 ** -7 * np.abs(a).max()

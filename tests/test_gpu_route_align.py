@@ -1,0 +1,174 @@
+"""GPU parity of the routing (moe_route) and index-list (moe_align) calls
+against the CPU oracle, through the C ABI."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import moe_workloads as wl
+from oracle import moe_oracle as mo
+from tests import helpers as h
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import mixture_experts_ffn_renorm_amd as moe
+    return moe
+
+
+# ---------------------------------------------------------------------------
+# align on fixed topk_ids: bit-exact
+# ---------------------------------------------------------------------------
+
+def run_align(ids: np.ndarray, E: int, B: int):
+    import torch
+    moe = _moe()
+    s, e, off, cnt = moe.moe_align(h.dev_i32(ids), E, B)
+    torch.cuda.synchronize()
+    off = off.cpu().numpy()
+    nb = int(off[E])
+    return (s.cpu().numpy()[: nb * B], e.cpu().numpy()[:nb], off, cnt.cpu().numpy())
+
+
+def check_align(ids: np.ndarray, E: int, B: int):
+    ref = mo.align(ids, E, B)
+    s, e, off, cnt = run_align(ids, E, B)
+    assert np.array_equal(off, ref["expert_block_offsets"])
+    assert np.array_equal(cnt, ref["expert_counts"])
+    assert np.array_equal(e, ref["expert_ids"])
+    assert np.array_equal(s, ref["sorted_token_ids"])
+
+
+def test_align_page_toy():
+    """The page's toy batch (M=3, E=4, top_k=2, BLOCK_SIZE_M=4), completed."""
+    ids = np.array([[2, 0], [0, 3], [1, 2]], dtype=np.int32)
+    s, e, off, cnt = run_align(ids, 4, 4)
+    assert s[:4].tolist() == [1, 2, 6, 6] and e[0] == 0
+    assert s.tolist() == [1, 2, 6, 6, 4, 6, 6, 6, 0, 5, 6, 6, 3, 6, 6, 6]
+    assert e.tolist() == [0, 1, 2, 3] and off.tolist() == [0, 1, 2, 3, 4]
+    check_align(ids, 4, 4)
+
+
+SHAPES = [(3, 2, 4), (1, 8, 128), (64, 8, 128), (37, 4, 60), (16, 4, 60),
+          (4096, 8, 128), (8192, 8, 256), (1, 1, 1), (100, 3, 7)]
+
+
+@pytest.mark.parametrize("pattern", ["random", "round_robin", "sparse", "one_expert_heavy"])
+@pytest.mark.parametrize("M,k,E", SHAPES)
+def test_align_patterns(pattern, M, k, E):
+    if k > E:
+        pytest.skip("top_k > E")
+    ids = wl.make_topk_ids(M, k, E, seed=1000 + M + E, pattern=pattern)
+    for B in (1, 4, 16, 32, 64, 128):
+        check_align(ids, E, B)
+
+
+def test_align_all_pairs_one_expert():
+    ids = np.zeros((1000, 1), dtype=np.int32)
+    for B in (1, 16, 128):
+        check_align(ids, 8, B)
+    ids = np.full((777, 1), 59, dtype=np.int32)
+    check_align(ids, 60, 16)
+
+
+def test_align_max_size():
+    """512 experts, 524,288 pairs (the largest expert count supported)."""
+    ids = wl.make_topk_ids(65536, 8, 512, seed=7)
+    for B in (16, 128):
+        check_align(ids, 512, B)
+
+
+def test_align_deterministic():
+    ids = wl.make_topk_ids(8192, 8, 256, seed=3)
+    a = run_align(ids, 256, 128)
+    b = run_align(ids, 256, 128)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+def run_route(lay, renormalize=None, top_k=None):
+    import torch
+    moe = _moe()
+    k = lay["top_k"] if top_k is None else top_k
+    ren = lay["renormalize"] if renormalize is None else renormalize
+    x, wr = h.dev_bf16(lay["x"]), h.dev_bf16(lay["w_router"])
+    bias = None if lay.get("logit_bias") is None else h.dev_f32(lay["logit_bias"])
+    M, E = lay["x"].shape[0], lay["w_router"].shape[0]
+    logits = torch.empty((M, E), dtype=torch.float32, device="cuda")
+    ids, wts = moe.moe_route(x, wr, k, ren, logit_bias=bias, logits_out=logits)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64), logits.cpu().numpy()
+
+
+def check_route(lay, renormalize=None, top_k=None, min_pass=0.9):
+    k = lay["top_k"] if top_k is None else top_k
+    ren = lay["renormalize"] if renormalize is None else renormalize
+    ids, wts, logits = run_route(lay, ren, k)
+    ref = mo.route(lay["x"], lay["w_router"], k, ren, lay.get("logit_bias"))
+    lref = ref["logits"]
+    assert np.abs(logits - lref).max() <= 1e-4 * max(1.0, np.abs(lref).max())
+    ok = ref["margin"] > h.MARGIN
+    assert ok.mean() >= min_pass
+    assert np.array_equal(ids[ok], ref["topk_ids"][ok])
+    assert np.abs(wts[ok] - ref["topk_weights"][ok]).max() <= h.WEIGHT_TOL
+    if ren:
+        assert np.abs(wts.sum(axis=1) - 1.0).max() <= 1e-6 * k
+    # every token: distinct ids in range, weights non-increasing
+    assert np.all((ids >= 0) & (ids < lay["w_router"].shape[0]))
+    assert all(len(set(r)) == k for r in ids.tolist())
+    assert np.all(np.diff(wts, axis=1) <= 1e-7)
+    # near-tie tokens: every chosen id is within the margin of the k-th logit
+    if (~ok).any():
+        kth = -np.sort(-ref["logits_f32"][~ok], axis=1)[:, k - 1]
+        chosen = np.take_along_axis(ref["logits_f32"][~ok], ids[~ok].astype(np.int64), axis=1)
+        assert np.all(chosen >= kth[:, None] - 2 * h.MARGIN)
+
+
+ROUTE_CASES = [("toy", 3), ("qwen3_decode", 1), ("qwen3_decode", 64), ("qwen3_prefill", 4096),
+               ("qwen15", 16), ("qwen15", 2048), ("wide256", 8), ("wide256", 8192)]
+
+
+@pytest.mark.parametrize("name,M", ROUTE_CASES)
+def test_route_workloads(name, M):
+    lay = wl.make_layer(name, M, I=8)   # same x and router as the full layer
+    check_route(lay)
+
+
+def test_route_no_renormalize():
+    check_route(wl.make_layer("qwen15", 512, I=8), renormalize=False)
+    check_route(wl.make_layer("toy", 3), renormalize=False)
+
+
+def test_route_k_equals_E_and_k1():
+    lay = wl.make_layer("toy", 3)
+    check_route(lay, top_k=4)
+    check_route(lay, top_k=1)
+    check_route(wl.make_layer("wide256", 64, I=8), top_k=1)
+
+
+def test_route_exact_ties_lower_id():
+    lay = wl.make_layer("toy", 9, E=6, top_k=3, H=64, I=8, seed=5)
+    lay["w_router"][4] = lay["w_router"][1]
+    lay["w_router"][5] = lay["w_router"][1]
+    ids, wts, logits = run_route(lay, True, 3)
+    assert np.array_equal(logits[:, 1], logits[:, 4]) and np.array_equal(logits[:, 1], logits[:, 5])
+    for t in range(9):
+        row = ids[t].tolist()
+        tied = [e for e in row if e in (1, 4, 5)]
+        assert tied == sorted(tied)     # lower id first among equal logits
+        order = np.lexsort((np.arange(6), -logits[t]))[:3]
+        assert row == order.tolist()
+
+
+def test_route_deterministic():
+    lay = wl.make_layer("qwen3_prefill", 4096, I=8)
+    a = run_route(lay)
+    b = run_route(lay)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
