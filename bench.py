@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X.
+
+A step is one moe_forward call (route -> align -> GEMM 1 + SiLU*up -> GEMM 2 +
+combine) on one batch of M tokens.  Steps cycle through L distinct synthetic
+layers held in HBM (weights drawn on the device), so the 256 MB Infinity
+Cache cannot serve the weights from one step to the next.  Inputs are
+resident in HBM before the timed region starts.
+
+Prints ONE JSON line:
+  value            tokens/s of the whole layer (M * steps / elapsed)
+  roofline         the dominant kernel's algorithmic bytes (or flops) per
+                   launch / its mean launch time (HIP events on the stream it
+                   runs on), against the MI355X peak
+  cpu_baseline     the CPU oracle on a bounded sample of the same workload
+  kernels          mean duration of every kernel of the step (events)
+Default workload: the Qwen3-30B-A3B-shaped decode layer (E=128, top_k=8,
+H=2048, I=768) at M=64 tokens.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+
+DEFAULT_WORKLOAD = ("qwen3_decode", 64)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    help="name:M, e.g. qwen3_prefill:4096 (default qwen3_decode:64)")
+    ap.add_argument("--layers", type=int, default=16, help="distinct layers cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration runs)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute)
+# ---------------------------------------------------------------------------
+
+def algorithmic(shape, M, touched):
+    """Per-forward algorithmic bytes and flops, and those of each GEMM.
+
+    touched = number of experts with at least one pair.
+      layer bytes  = touched*6*H*I (W13 + W2, bf16) + 2*E*H (router) + 4*M*H (x in, out)
+      GEMM 1 bytes = touched*4*H*I (W13) + 2*M*H (x) + 2*P*I (act out)
+      GEMM 2 bytes = touched*2*H*I (W2) + 2*P*I (act in) + 4*P (weights) + 2*M*H (out)
+      layer flops  = 6*H*I*P + 2*M*H*E;  GEMM 1 flops = 4*H*I*P;  GEMM 2 flops = 2*H*I*P
+    """
+    E, k, H, I = shape.E, shape.top_k, shape.H, shape.I
+    P = M * k
+    return dict(
+        layer_bytes=touched * 6 * H * I + 2 * E * H + 4 * M * H,
+        layer_flops=6 * H * I * P + 2 * M * H * E,
+        gemm1_bytes=touched * 4 * H * I + 2 * M * H + 2 * P * I,
+        gemm1_flops=4 * H * I * P,
+        gemm2_bytes=touched * 2 * H * I + 2 * P * I + 4 * P + 2 * M * H,
+        gemm2_flops=2 * H * I * P,
+    )
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; a stored counter profile is valid only for it."""
+    import glob
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_ffn_renorm_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_key, kernel):
+    """HBM traffic per launch of `kernel` from the committed counter summary
+    (profiles/counters_<workload>.md), or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload_key}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{kernel}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+# ---------------------------------------------------------------------------
+# the run
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (multi-GPU sharding is described as design, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_workloads as wl
+    import mixture_experts_ffn_renorm_amd as moe
+
+    name, M = DEFAULT_WORKLOAD
+    if args.workload:
+        name, m = args.workload.split(":")
+        M = int(m)
+    shape = wl.WORKLOADS[name]
+    E, k, H, I = shape.E, shape.top_k, shape.H, shape.I
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = moe.library()
+    stream = torch.cuda.current_stream()
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- inputs resident in HBM: L distinct layers, one batch of x ----
+    L = max(1, args.layers)
+    layers = [wl.make_device_layer(shape, M, layer=i + 1, device=dev) for i in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_for(shape, M))
+    x = torch.randn((M, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((M, k), dtype=torch.float32, device=dev)
+    ws = moe.workspace(M, E, k, H, I, dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        lay = layers[i % L]
+        return moe.moe_forward(x, lay["w_router"], lay["w13"], lay["w2"], k,
+                               shape.renormalize, logit_bias=lay["logit_bias"], out=out,
+                               topk_ids_out=ids, topk_weights_out=wts, ws=ws, stream=stream)
+
+    # touched experts per layer (from each layer's own routing)
+    touched = []
+    for i in range(L):
+        _, info = step(i)
+        touched.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+    mean_touched = float(np.mean(touched))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens_per_s = M * args.steps / elapsed
+
+    # ---- per-kernel times: the same work as separate C-ABI calls with HIP
+    #      events between them on the launch stream ----
+    B = moe.moe_pick_block_m(M, E, k)
+    cap, nbl = moe.align_capacity(M * k, E, B)
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    eids = torch.empty(max(nbl, 1), dtype=torch.int32, device=dev)
+    boff = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    act = torch.empty((M * k, I), dtype=torch.bfloat16, device=dev)
+    logits = torch.empty((M, E), dtype=torch.float32, device=dev)
+    align_ws = torch.empty(max(moe.moe_align_workspace_size(M, k, E), 16), dtype=torch.uint8,
+                           device=dev)
+    names = ["route", "align", "gemm1", "gemm2"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def staged(i, ev=None):
+        lay = layers[i % L]
+        if ev: ev[0].record(stream)
+        moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
+                      topk_ids=ids, topk_weights=wts, logits_out=logits, stream=stream)
+        if ev: ev[1].record(stream)
+        moe.moe_align(ids, E, B, sorted_ids, eids, boff, counts, ws=align_ws, stream=stream)
+        if ev: ev[2].record(stream)
+        moe.moe_grouped_gemm_w13_act(x, lay["w13"], sorted_ids, eids, boff, k, B, act=act,
+                                     stream=stream)
+        if ev: ev[3].record(stream)
+        moe.moe_grouped_gemm_w2_combine(act, lay["w2"], wts, sorted_ids, eids, boff, M, k, B,
+                                        out=out, ws=ws, stream=stream)
+        if ev: ev[4].record(stream)
+
+    for i in range(min(args.warmup, 10)):
+        staged(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        staged(i, evs[i])
+    torch.cuda.synchronize()
+    kern_us = {n: 1e3 * float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                        for i in range(args.steps)]))
+               for j, n in enumerate(names)}
+
+    work = algorithmic(shape, M, mean_touched)
+    variant = "stream" if B == 16 else "tiled"
+    # dominant kernel: GEMM 1 (2/3 of the weight bytes and of the flops)
+    mfma_bound = variant == "tiled" and work["gemm1_flops"] / work["gemm1_bytes"] > \
+        1e3 * BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 0.5
+    t_g1 = kern_us["gemm1"] * 1e-6
+    workload_key = f"{name}_M{M}"
+    if mfma_bound:
+        achieved = work["gemm1_flops"] / t_g1 / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = work["gemm1_bytes"] / t_g1 / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = f"gemm1_{variant}"
+    roof["mean_launch_us"] = round(kern_us["gemm1"], 2)
+    roof["algorithmic_bytes_per_launch"] = int(work["gemm1_bytes"])
+    roof["traffic"] = stored_traffic(workload_key, f"gemm1_{variant}")
+
+    layer_s = ms_per_step * 1e-3
+    result = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "description": shape.description, "M": M, "E": E,
+                   "top_k": k, "H": H, "I": I, "renormalize": shape.renormalize,
+                   "layers_cycled": L, "block_m": B, "variant": variant,
+                   "mean_touched_experts": mean_touched},
+        "layer": {"alg_bytes": int(work["layer_bytes"]), "alg_flops": int(work["layer_flops"]),
+                  "hbm_frac": round(work["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(work["layer_flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": roof,
+    }
+
+    # ---- decode sweep (same shape, smaller batches) ----
+    if not args.no_sweep and name == "qwen3_decode":
+        sweep = {}
+        for Ms in (1, 8):
+            xs = x[:Ms].contiguous()
+            outs = torch.empty((Ms, H), dtype=torch.bfloat16, device=dev)
+            for i in range(args.warmup):
+                lay = layers[i % L]
+                moe.moe_forward(xs, lay["w_router"], lay["w13"], lay["w2"], k, True,
+                                out=outs, ws=ws, stream=stream)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                lay = layers[i % L]
+                moe.moe_forward(xs, lay["w_router"], lay["w13"], lay["w2"], k, True,
+                                out=outs, ws=ws, stream=stream)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / args.steps
+            sweep[f"M={Ms}"] = {"tokens_per_s": round(Ms / dt, 1), "us_per_layer": round(1e6 * dt, 2)}
+        result["decode_sweep"] = sweep
+
+    # ---- the oracle on the host, on a bounded sample ----
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shape, M, layers[0], x)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(shape, M, lay, x):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload: layer 0 of the cycle, the first S tokens of the batch (S chosen
+    so the oracle runs roughly 10-30 s), tokens/s = S / wall time."""
+    import numpy as np
+    import torch
+
+    from oracle import moe_oracle as mo
+
+    def bits(t):
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    S = min(M, 64)
+    host = dict(x=bits(x[:S]), w_router=bits(lay["w_router"]), w13=bits(lay["w13"]),
+                w2=bits(lay["w2"]),
+                logit_bias=None if lay["logit_bias"] is None else lay["logit_bias"].cpu().numpy(),
+                M=S, E=shape.E, top_k=shape.top_k, H=shape.H, I=shape.I,
+                renormalize=shape.renormalize)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 1) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    mo.forward(host)
+    dt = time.perf_counter() - t0
+    return {"value": round(S / dt, 3), "unit": "tokens/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{S} tokens of layer 0 ({shape.name}, M={M}); numpy float64 oracle, "
+                      f"{dt:.2f} s wall",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

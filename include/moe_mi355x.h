@@ -97,8 +97,8 @@ int moe_pick_block_m(int M, int E, int top_k);
  *   topk_weights [M, top_k] fp32  out: the kept softmax probabilities,
  *                                 rescaled to sum 1 if renormalize != 0
  *   logits_out   [M, E] fp32 or NULL  out: the fp32 logits (+ bias)
- *   workspace    device scratch of ws_bytes >= moe_workspace_size(M, E,
- *                top_k, 8, 8); may be NULL when logits_out is given.
+ *   workspace    device scratch of ws_bytes >= M*E*4 (holds the logits when
+ *                logits_out is NULL; may be NULL when logits_out is given).
  * Logits accumulate bf16 x bf16 products in fp32; the top-k decision is
  * taken on those fp32 values.
  */
@@ -126,11 +126,16 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bi
  *                        entry E = num_blocks.  It stays in device memory;
  *                        later calls read it there, so no host sync is needed.
  *   expert_counts        out [E] int32 (pairs per expert) or NULL.
+ *   workspace            device scratch of ws_bytes >=
+ *                        moe_align_workspace_size(M, top_k, E) (that size is
+ *                        0 for small batches; NULL is then allowed).
  * The result is deterministic (the same bits on every run).
  */
+size_t moe_align_workspace_size(int M, int top_k, int E);
 int moe_align(const int32_t* topk_ids, int M, int top_k, int E, int block_m,
               int32_t* sorted_token_ids, int32_t* expert_ids,
-              int32_t* expert_block_offsets, int32_t* expert_counts, void* stream);
+              int32_t* expert_block_offsets, int32_t* expert_counts,
+              void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_gemm_w13_act -- grouped GEMM 1 with SiLU(gate)*up fused.

@@ -49,8 +49,9 @@ _SIGNATURES = {
     "moe_route": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                            _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                            _c_void_p]),
+    "moe_align_workspace_size": (_c_size_t, [_c_int] * 3),
     "moe_align": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
-                           _c_void_p, _c_void_p, _c_void_p]),
+                           _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "moe_grouped_gemm_w13_act": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
                                  [_c_void_p, ctypes.POINTER(DispatchInfo), _c_void_p]),
     "moe_grouped_gemm_w2_combine": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 +
@@ -183,8 +184,12 @@ def align_capacity(P: int, E: int, block_m: int) -> tuple:
     return P + nz * (block_m - 1), -(-P // block_m) + nz
 
 
+def moe_align_workspace_size(M: int, top_k: int, E: int) -> int:
+    return int(library().moe_align_workspace_size(M, top_k, E))
+
+
 def moe_align(topk_ids, E: int, block_m: int, sorted_token_ids=None, expert_ids=None,
-              expert_block_offsets=None, expert_counts=None, stream=None):
+              expert_block_offsets=None, expert_counts=None, ws=None, stream=None):
     torch = _torch()
     M, top_k = topk_ids.shape
     _check(topk_ids, "topk_ids", (torch.int32,))
@@ -206,9 +211,13 @@ def moe_align(topk_ids, E: int, block_m: int, sorted_token_ids=None, expert_ids=
     if sorted_token_ids.numel() < cap or expert_ids.numel() < nbl or \
             expert_block_offsets.numel() < E + 1 or expert_counts.numel() < E:
         raise ValueError("moe_align output buffers are too small")
+    need = moe_align_workspace_size(M, top_k, E)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     st = library().moe_align(_ptr(topk_ids), M, top_k, E, block_m, _ptr(sorted_token_ids),
                              _ptr(expert_ids), _ptr(expert_block_offsets),
-                             _ptr(expert_counts), _stream(stream))
+                             _ptr(expert_counts), _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream))
     _raise("moe_align", st)
     return sorted_token_ids, expert_ids, expert_block_offsets, expert_counts
 

@@ -3,20 +3,23 @@
 // section "How vLLM runs the layer: two index lists and no copies",
 // sub-section "The two index lists": pair ids sorted by expert, each group
 // padded with the id P = M*top_k to a multiple of BLOCK_SIZE_M, one expert
-// per block.  The page leaves the order inside a group open; this kernel
-// fixes it to ascending pair id, which makes the result deterministic.
+// per block.  The page leaves the order inside a group open; these kernels
+// fix it to ascending pair id, which makes the result deterministic.
 //
-// One workgroup of 16 waves does the whole job in LDS:
-//   1. each wave counts the experts of one contiguous segment of pairs into
-//      its own LDS histogram;
-//   2. per expert: n_e, blocks ceil(n_e / B), exclusive scan over experts
-//      -> block offsets; per (wave, expert) start position = expert start +
-//      pairs of that expert in earlier segments;
-//   3. stable scatter: each wave walks its segment 64 pairs at a time; a
-//      pair's rank among earlier lanes with the same expert comes from a
-//      ballot per id bit (AND of matching ballots) and a popcount;
-//   4. expert id of every block and the pad entries (binary search of the
-//      block offsets).
+// The pairs are cut into G contiguous segments, one per workgroup of 16
+// waves, and each segment into 16 contiguous wave pieces.  Counting uses a
+// ballot per expert-id bit: the lanes of a 64-pair chunk that hold the same
+// expert form one group (AND of matching ballots), so a chunk costs one LDS
+// atomic per distinct expert rather than one per pair, and a pair's rank
+// among the earlier pairs of its chunk with the same expert is a popcount.
+//
+//   G > 1:  align_count writes each segment's per-expert counts to scratch;
+//           align_scatter then, in every workgroup, rebuilds the per-expert
+//           block offsets (exclusive scan over experts), the start of its
+//           own segment inside each expert group, recounts its segment per
+//           wave, and scatters its pairs stably.
+//   G == 1: align_scatter alone (counts come from its own segment).
+// Block experts and pad entries are then filled by all workgroups.
 #include "moe_common.h"
 
 using namespace moe;
@@ -25,6 +28,33 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
+
+// Lanes of the wave whose (valid) id equals this lane's id.
+__device__ __forceinline__ unsigned long long match_lanes(int id, bool valid, int nbits) {
+  unsigned long long m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (id >> b) & 1;
+    const unsigned long long bb = __ballot(valid && bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__device__ __forceinline__ int id_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// Count the experts of pairs [s0, s1) into hist[E] (LDS), one wave.
+__device__ __forceinline__ void count_piece(const int32_t* __restrict__ ids, int s0, int s1,
+                                            int* hist, int nbits) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int base = s0; base < s1; base += 64) {
+    const int p = base + lane;
+    const bool valid = p < s1;
+    const int id = valid ? ids[p] : 0;
+    const unsigned long long m = match_lanes(id, valid, nbits);
+    if (valid && (m & below) == 0ull) atomicAdd(&hist[id], __popcll(m));
+  }
+}
 
 __device__ __forceinline__ int block_scan_exclusive(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -58,40 +88,80 @@ __device__ __forceinline__ int expert_of_block(const int* boff, int E, int blk) 
   return lo;
 }
 
-__global__ __launch_bounds__(kThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int B, int32_t* __restrict__ sorted,
+struct Seg {
+  int s0, s1;   // this workgroup's pairs
+  int w0, w1;   // this wave's pairs
+};
+
+__device__ __forceinline__ Seg segment(int P, int G) {
+  Seg s;
+  const int seg = ceil_div(ceil_div(P, G), 64) * 64;
+  s.s0 = min(P, (int)blockIdx.x * seg);
+  s.s1 = min(P, s.s0 + seg);
+  const int piece = ceil_div(ceil_div(s.s1 - s.s0, kWaves), 64) * 64;
+  const int w = threadIdx.x >> 6;
+  s.w0 = min(s.s1, s.s0 + w * piece);
+  s.w1 = min(s.s1, s.w0 + piece);
+  return s;
+}
+
+// grid G (> 1): per-segment expert counts -> seg_counts[G][E]
+__global__ __launch_bounds__(kThreads) void align_count_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int G, int32_t* __restrict__ seg_counts) {
+  extern __shared__ int hist[];   // [E]
+  for (int i = threadIdx.x; i < E; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const Seg sg = segment(P, G);
+  count_piece(ids, sg.w0, sg.w1, hist, id_bits(E));
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += kThreads)
+    seg_counts[(size_t)blockIdx.x * E + i] = hist[i];
+}
+
+// grid G: offsets, stable scatter of this segment, block experts and pads.
+__global__ __launch_bounds__(kThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int B, int G,
+    const int32_t* __restrict__ seg_counts, int32_t* __restrict__ sorted,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ boff_out,
     int32_t* __restrict__ counts_out) {
   extern __shared__ int smem[];
-  int* hist = smem;                   // [kWaves][E]  counts, then running positions
-  int* boff = hist + kWaves * E;      // [E + 1]
-  int* cnt = boff + E + 1;            // [E]
-  int* wave_tot = cnt + E;            // [kWaves]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int* hist = smem;                  // [kWaves][E] counts, then running positions
+  int* boff = hist + kWaves * E;     // [E + 1]
+  int* cnt = boff + E + 1;           // [E]
+  int* wave_tot = cnt + E;           // [kWaves]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int nbits = id_bits(E);
 
   for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
   __syncthreads();
-
-  // 1. per-wave histograms of contiguous segments (segment length multiple of 64)
-  const int seg = ceil_div(ceil_div(P, kWaves), 64) * 64;
-  const int s0 = min(P, w * seg), s1 = min(P, s0 + seg);
-  for (int p = s0 + lane; p < s1; p += 64) atomicAdd(&hist[w * E + ids[p]], 1);
+  const Seg sg = segment(P, G);
+  count_piece(ids, sg.w0, sg.w1, hist + w * E, nbits);
   __syncthreads();
 
-  // 2. counts, block offsets, per-(wave, expert) start positions
-  int n_e = 0, nb = 0;
+  // expert totals, block offsets, start of every (wave, expert) run
+  int n_e = 0, before = 0;
   if (tid < E) {
-    for (int i = 0; i < kWaves; ++i) n_e += hist[i * E + tid];
-    nb = ceil_div(n_e, B);
+    if (G > 1) {
+      for (int i = 0; i < G; ++i) {
+        const int c = seg_counts[(size_t)i * E + tid];
+        n_e += c;
+        if (i < (int)blockIdx.x) before += c;
+      }
+    } else {
+      for (int i = 0; i < kWaves; ++i) n_e += hist[i * E + tid];
+    }
   }
+  const int nb = tid < E ? ceil_div(n_e, B) : 0;
   int total_blocks = 0;
   const int excl = block_scan_exclusive(nb, wave_tot, total_blocks);
   if (tid < E) {
     boff[tid] = excl;
     cnt[tid] = n_e;
-    boff_out[tid] = excl;
-    if (counts_out != nullptr) counts_out[tid] = n_e;
-    int run = excl * B;
+    if (blockIdx.x == 0) {
+      boff_out[tid] = excl;
+      if (counts_out != nullptr) counts_out[tid] = n_e;
+    }
+    int run = excl * B + before;
     for (int i = 0; i < kWaves; ++i) {
       const int c = hist[i * E + tid];
       hist[i * E + tid] = run;
@@ -100,24 +170,18 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   }
   if (tid == 0) {
     boff[E] = total_blocks;
-    boff_out[E] = total_blocks;
+    if (blockIdx.x == 0) boff_out[E] = total_blocks;
   }
   __syncthreads();
 
-  // 3. stable scatter, 64 pairs at a time per wave, in pair order
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  // stable scatter, 64 pairs at a time per wave, in pair order
   const unsigned long long below = (1ull << lane) - 1ull;
   int* my_start = hist + w * E;
-  for (int base = s0; base < s1; base += 64) {
+  for (int base = sg.w0; base < sg.w1; base += 64) {
     const int p = base + lane;
-    const bool valid = p < s1;
+    const bool valid = p < sg.w1;
     const int id = valid ? ids[p] : 0;
-    unsigned long long match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (id >> b) & 1;
-      const unsigned long long bb = __ballot(valid && bit);
-      match &= bit ? bb : ~bb;
-    }
+    const unsigned long long match = match_lanes(id, valid, nbits);
     const int rank = __popcll(match & below);
     const int size = __popcll(match);
     int pos = 0;
@@ -131,11 +195,12 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     __builtin_amdgcn_wave_barrier();
   }
 
-  // 4. expert of each block, pad entries
-  for (int blk = tid; blk < total_blocks; blk += kThreads)
+  // expert of each block and the pad entries, split over the workgroups
+  const int gtid = blockIdx.x * kThreads + tid, gstride = G * kThreads;
+  for (int blk = gtid; blk < total_blocks; blk += gstride)
     expert_ids[blk] = expert_of_block(boff, E, blk);
   const int nslots = total_blocks * B;
-  for (int pos = tid; pos < nslots; pos += kThreads) {
+  for (int pos = gtid; pos < nslots; pos += gstride) {
     const int blk = pos / B;
     const int e = expert_of_block(boff, E, blk);
     if (pos - boff[e] * B >= cnt[e]) sorted[pos] = P;
@@ -146,11 +211,28 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 
 namespace moe_host {
 
+int align_segments(int P) {
+  const int g = (P + kAlignPairsPerSegment - 1) / kAlignPairsPerSegment;
+  return g < 1 ? 1 : (g > kAlignMaxSegments ? kAlignMaxSegments : g);
+}
+
+size_t align_scratch_bytes(int P, int E) {
+  const int G = align_segments(P);
+  return G > 1 ? (size_t)G * E * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_align(const AlignArgs& a, hipStream_t s) {
+  const int G = align_segments(a.P);
+  if (G > 1) {
+    hipLaunchKernelGGL(align_count_kernel, dim3(G), dim3(kThreads), sizeof(int) * a.E, s,
+                       a.topk_ids, a.P, a.E, G, a.scratch);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const size_t lds = sizeof(int) * ((size_t)kWaves * a.E + (a.E + 1) + a.E + kWaves);
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), lds, s, a.topk_ids, a.P, a.E,
-                     a.block_m, a.sorted_token_ids, a.expert_ids, a.expert_block_offsets,
-                     a.expert_counts);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(G), dim3(kThreads), lds, s, a.topk_ids, a.P,
+                     a.E, a.block_m, G, a.scratch, a.sorted_token_ids, a.expert_ids,
+                     a.expert_block_offsets, a.expert_counts);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ long long sorted_capacity(long long P, int E, int B) {
 // The fp32 per-token sums and the arrival counters are adjacent so that one
 // pass clears both.
 struct Layout {
-  size_t ids, wts, logits, sorted, eids, boff, counts, act, acc, cnt, total;
+  size_t ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, acc, cnt, total;
   size_t zero_words;  // 4-byte words of acc + cnt
 };
 
@@ -52,6 +52,7 @@ Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
   L.eids = take((size_t)max_blocks(P, E, B) * 4);
   L.boff = take((size_t)(E + 1) * 4);
   L.counts = take((size_t)E * 4);
+  L.align_scratch = take(align_scratch_bytes((int)P, E));
   L.act = take((size_t)P * I * 2);
   L.total = off;
   return L;
@@ -159,17 +160,24 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bi
   return MOE_OK;
 }
 
+size_t moe_align_workspace_size(int M, int top_k, int E) {
+  if (check_sizes(M, E, top_k, 8, 8) != MOE_OK) return 0;
+  return align_scratch_bytes(M * top_k, E);
+}
+
 int moe_align(const int32_t* topk_ids, int M, int top_k, int E, int block_m,
               int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* expert_block_offsets,
-              int32_t* expert_counts, void* stream) {
+              int32_t* expert_counts, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_sizes(M, E, top_k, 8, 8);
   if (st != MOE_OK) return st;
   if (block_m < 1 || block_m > 256) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
   if (!topk_ids || !sorted_token_ids || !expert_ids || !expert_block_offsets)
     return MOE_ERR_INVALID_ARG;
+  const size_t need = align_scratch_bytes(M * top_k, E);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   AlignArgs a{topk_ids, M * top_k, E, block_m, sorted_token_ids, expert_ids,
-              expert_block_offsets, expert_counts};
+              expert_block_offsets, expert_counts, static_cast<int32_t*>(workspace)};
   MOE_TRY_HIP(launch_align(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
@@ -237,7 +245,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
-  fill_info(info, B, H, I, M == 0 ? 0 : 5);
+  fill_info(info, B, H, I, M == 0 ? 0 : 4 + (align_segments(M * top_k) > 1 ? 2 : 1));
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
   const Layout L = forward_layout(M, E, top_k, H, I, B);
@@ -257,7 +265,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   MOE_TRY_HIP(launch_route_logits(ra, s));
   MOE_TRY_HIP(launch_route_topk(ra, s));
   AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
-               reinterpret_cast<int32_t*>(ws + L.counts)};
+               reinterpret_cast<int32_t*>(ws + L.counts),
+               reinterpret_cast<int32_t*>(ws + L.align_scratch)};
   MOE_TRY_HIP(launch_align(aa, s));
   GemmArgs g = gemm_args(M, top_k, E, H, I, B);
   g.sorted_token_ids = sorted;

@@ -5,13 +5,14 @@
 // so the cost is the weight bytes and the kernel's job is to stream them at
 // full HBM bandwidth.
 //
-// Blocks of 16 pairs (index lists built with block_m = 16).  Each lane
-// streams one weight row directly from HBM into registers with 16-byte
-// loads: lane l owns row (l % 16) of a 16-row tile and, inside each
-// 256-element k super-chunk, the 64 contiguous elements [64 g, 64 g + 64)
-// with g = l / 16 (eight loads, one 128-byte run).  The gathered pair rows
-// are loaded with the same k map as the MFMA B operand, so one
-// 16x16x32 MFMA per 8 loaded elements does the dot products with no
+// Blocks of 16 pairs (index lists built with block_m = 16).  Weight rows
+// stream directly from HBM into registers with 16-byte loads in the MFMA
+// operand layout: lane l owns row (l % 16) of a 16-row tile, and for the
+// s-th 32-element k step of a 256-element super-chunk it loads elements
+// 32 s + 8 g .. + 7 (g = l / 16), so the four lanes of a row read 64
+// contiguous bytes per load instruction and consecutive instructions walk
+// along the row.  The gathered pair rows are loaded the same way as the B
+// operand, so one 16x16x32 MFMA per load does the dot products with no
 // cross-lane reduction.  Pads (id >= M*top_k) load zeros and store nothing.
 //
 // GEMM 1: a workgroup owns 16 gate rows and the matching 16 up rows of
@@ -30,7 +31,7 @@ using namespace moe;
 namespace {
 
 constexpr int kBM = 16;
-constexpr int kSC = 256;   // k elements per super-chunk (4 groups x 64)
+constexpr int kSC = 256;   // k elements per super-chunk (8 MFMA k steps of 32)
 
 __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
@@ -55,11 +56,11 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
   f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   const int nsc = ceil_div(H, kSC);
   for (int sc = wv; sc < nsc; sc += 4) {
-    const int kb = sc * kSC + g * 64;
+    const int kb = sc * kSC + g * 8;
     u32x4 ga[8], ua[8], xb[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int k = kb + s * 8;
+      const int k = kb + s * 32;
       const bool kin = k < H;
       ga[s] = load16_or_zero(gp + k, n_ok && kin);
       ua[s] = load16_or_zero(up + k, n_ok && kin);
@@ -114,11 +115,11 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int nsc = ceil_div(I, kSC);
   for (int sc = 0; sc < nsc; ++sc) {
-    const int kb = sc * kSC + g * 64;
+    const int kb = sc * kSC + g * 8;
     u32x4 wa[8], ab[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int k = kb + s * 8;
+      const int k = kb + s * 32;
       const bool kin = k < I;
       wa[s] = load16_or_zero(wp + k, h_ok && kin);
       ab[s] = load16_or_zero(ap + k, p_ok && kin);
@@ -137,7 +138,11 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(
     for (int q = 0; q < 4; ++q) unsafeAtomicAdd(dst + q, wt * acc[q]);
   }
 
-  __threadfence();
+  // Every wave waits until its additions are performed, then the workgroup
+  // counts one arrival per (token, 64 columns).  The last of the top_k
+  // arrivals reads the finished sums with atomic exchanges (served where
+  // the additions were performed; they also leave the sums at zero).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int ncg = ceil_div(H, 64);
   if (threadIdx.x < kBM) {
@@ -151,14 +156,12 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(
     s_last[threadIdx.x] = last;
   }
   __syncthreads();
-  __threadfence();
   for (int it = wv; it < kBM; it += 4) {
     const int t = s_last[it];
     if (t < 0) continue;
     const int col = blockIdx.y * 64 + lane;
     if (col < H) {
-      const float v = __hip_atomic_load(accum + (size_t)t * H + col, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+      const float v = atomicExch(accum + (size_t)t * H + col, 0.0f);
       out[(size_t)t * H + col] = (uint16_t)f32_to_bf16(v);
     }
   }

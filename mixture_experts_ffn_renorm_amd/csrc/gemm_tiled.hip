@@ -203,9 +203,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm)
     }
   }
 
-  // ---- last arrival per (token, 64-column group) writes the bf16 row piece ----
+  // ---- last arrival per (token, 64-column group) writes the bf16 row piece.
+  // Every wave waits until its additions are performed, then the workgroup
+  // counts its arrivals; the last of the top_k arrivals reads the finished
+  // sums with atomic exchanges (served where the additions were performed;
+  // they also leave the sums at zero).
   __shared__ int s_last[2 * BM];
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int ncg = ceil_div(H, 64);
   if (tid < 2 * BM) {
@@ -221,14 +225,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm)
     s_last[tid] = last;
   }
   __syncthreads();
-  __threadfence();
   for (int it = wv; it < 2 * BM; it += 4) {
     const int t = s_last[it];
     if (t < 0) continue;
     const int col = (nt * 2 + it / BM) * 64 + lane;
     if (col < H) {
-      const float v = __hip_atomic_load(prm.acc + (size_t)t * H + col, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+      const float v = atomicExch(prm.acc + (size_t)t * H + col, 0.0f);
       prm.out[(size_t)t * H + col] = (uint16_t)f32_to_bf16(v);
     }
   }

@@ -113,7 +113,12 @@ struct AlignArgs {
   int32_t* expert_ids;
   int32_t* expert_block_offsets;
   int32_t* expert_counts;  // may be null
+  int32_t* scratch;        // align_scratch_bytes(P, E) bytes (null when 0)
 };
+constexpr int kAlignPairsPerSegment = 2048;  // pairs per align workgroup
+constexpr int kAlignMaxSegments = 64;
+int align_segments(int P);
+size_t align_scratch_bytes(int P, int E);
 hipError_t launch_align(const AlignArgs& a, hipStream_t s);
 
 struct GemmArgs {

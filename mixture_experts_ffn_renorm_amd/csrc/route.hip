@@ -9,16 +9,21 @@ using namespace moe;
 
 namespace {
 
-constexpr int kTokTile = 16;     // tokens per workgroup (MFMA B columns)
-constexpr int kExpTile = 64;     // experts per workgroup (4 waves x 16 rows)
-constexpr int kKChunk = 128;     // k elements per lane-group sweep (4 MFMAs)
+constexpr int kTokTile = 16;     // tokens per MFMA tile (B columns)
 
-// grid: (ceil(M/16), ceil(E/64)); block: 256 threads.
-// Wave w computes logits of experts e0 = by*64 + 16w .. +15 for the 16 tokens
-// of the tile.  Lane l: row/col r = l % 16, k group g = l / 16.  Within a
-// 128-element k chunk the lane loads the 32 contiguous elements
-// [g*32, g*32+32) of its W_r row and of its token row; MFMA s (0..3) pairs
-// elements g*32 + 8s .. +7 of both, so each chunk is summed exactly once.
+// Router logits on the matrix cores, logits[t, e] = sum_h x[t, h] W_r[e, h]
+// (+ bias[e]), fp32 accumulation of exact bf16 products.  W_r rows are the
+// A operand, token rows the B operand; lane l (row/column r = l % 16, group
+// g = l / 16) loads elements k0 + 8 g .. + 7 of its row for the 32-element
+// k step at k0, so the four lanes of a row read 64 contiguous bytes.
+//
+// kSplitK = true  (small batches): a workgroup owns 16 tokens x 16 experts
+//   and its 4 waves split K in four contiguous ranges; partial tiles are
+//   added through LDS.  Many workgroups read W_r in parallel.
+// kSplitK = false (large batches): a workgroup owns 16 tokens x 64 experts,
+//   wave w the 16 experts 16 w .. 16 w + 15 over the whole K.
+// grid: (ceil(M / 16), ceil(E / experts per workgroup)); block: 256.
+template <bool kSplitK>
 __global__ __launch_bounds__(256) void route_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
@@ -35,29 +40,45 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
     for (size_t i = (n4 << 2) + wg * 256 + threadIdx.x; i < zero_words; i += nwg * 256)
       zero_ptr[i] = 0.0f;
   }
-
+  __shared__ f32x4 red[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kTokTile;
-  const int e0 = blockIdx.y * kExpTile + w * 16;
-  if (e0 >= E) return;
+  const int e0 = kSplitK ? blockIdx.y * 16 : blockIdx.y * 64 + w * 16;
   const int erow = e0 + r, trow = t0 + r;
   const bool e_ok = erow < E, t_ok = trow < M;
   const uint16_t* ap = wr + (size_t)(e_ok ? erow : 0) * H;
   const uint16_t* bp = x + (size_t)(t_ok ? trow : 0) * H;
+  int kbeg = 0, kend = H;
+  if (kSplitK) {
+    const int kw = ceil_div(ceil_div(H, 4), 32) * 32;
+    kbeg = min(H, w * kw);
+    kend = min(H, kbeg + kw);
+  }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < H; kc += kKChunk) {
-    u32x4 av[4], bv[4];
+  if (!kSplitK && e0 >= E) {
+    // no experts for this wave
+  } else {
+    constexpr int U = 8;   // k steps whose loads are in flight together
+    for (int k0 = kbeg; k0 < kend; k0 += 32 * U) {
+      u32x4 av[U], bv[U];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = kc + g * 32 + s * 8;
-      const bool kin = k < H;  // H % 8 == 0, so k < H means all 8 fit
-      av[s] = load16_or_zero(ap + k, e_ok && kin);
-      bv[s] = load16_or_zero(bp + k, t_ok && kin);
+      for (int s = 0; s < U; ++s) {
+        const int k = k0 + 32 * s + 8 * g;
+        const bool kin = k < kend;   // kend is H or a multiple of 32; H % 8 == 0
+        av[s] = load16_or_zero(ap + k, e_ok && kin);
+        bv[s] = load16_or_zero(bp + k, t_ok && kin);
+      }
+#pragma unroll
+      for (int s = 0; s < U; ++s) acc = mfma_16x16x32(av[s], bv[s], acc);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(av[s], bv[s], acc);
+  }
+  if (kSplitK) {
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w != 0) return;
+    acc = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
   }
   // C: lane holds experts e0 + 4g + q (q = 0..3) for token t0 + r.
   if (t_ok) {
@@ -73,69 +94,68 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   }
 }
 
-// One wave per token.  Lane l owns experts l, l+64, ... (E <= 512).
-// Softmax over all E (fp32, max-shifted), then k rounds of a wave argmax on
-// (logit desc, expert id asc); the probability of the winner is
-// exp(l - max) / sum.  Renormalize divides by the sum of the k kept values.
+// Softmax over all E, ordered top-k, renormalize; one wave per token.
+// The token's logits sit in LDS; each lane ranks its own values against all
+// E (rank = number of larger logits, equal logits ordered by expert id), and
+// a value of rank j < k is slot j.  Slot 0 is the largest; exact ties go to
+// the lower expert id.  The probability of a kept expert is
+// exp(l - max) / sum over all E of exp(l' - max); renormalize divides the
+// kept probabilities by their sum.
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int M, int E, int top_k, int renormalize,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= M) return;
-  constexpr int kMaxPerLane = 8;
-  float v[kMaxPerLane];
+  constexpr int kMaxE = 512, kMaxPerLane = kMaxE / 64;
+  __shared__ __attribute__((aligned(16))) float s_log[4][kMaxE];
+  __shared__ float s_p[4][32];
+  __shared__ int s_id[4][32];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= M) return;   // whole wave; no workgroup barrier below
+  float* lw = s_log[w];
   const float* row = logits + (size_t)t * E;
+  float v[kMaxPerLane];
+  float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? row[e] : -INFINITY;
+    if (e < E) lw[e] = v[i];
+    m = fmaxf(m, v[i]);
   }
-  float m = v[0];
-#pragma unroll
-  for (int i = 1; i < kMaxPerLane; ++i) m = fmaxf(m, v[i]);
   m = wave_max(m);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i)
     if (lane + 64 * i < E) s += __expf(v[i] - m);
   s = wave_sum(s);
-
-  uint32_t taken = 0;
-  int my_id = 0;
-  float my_p = 0.f;
-  for (int j = 0; j < top_k; ++j) {
-    // best untaken candidate of this lane (ids increase with i, so strict >
-    // keeps the lower id on ties)
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7FFFFFFF)) {
-        bv = v[i];
-        bi = e;
-      }
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    if (e >= E) continue;
+    int rank = 0;
+    const float ve = v[i];
+    int j = 0;
+    for (; j + 4 <= E; j += 4) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(lw + j);
+      rank += (o[0] > ve) || (o[0] == ve && j + 0 < e);
+      rank += (o[1] > ve) || (o[1] == ve && j + 1 < e);
+      rank += (o[2] > ve) || (o[2] == ve && j + 2 < e);
+      rank += (o[3] > ve) || (o[3] == ve && j + 3 < e);
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, kWave);
-      const int oi = __shfl_xor(bi, d, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      my_id = bi;
-      my_p = __expf(bv - m) / s;
+    for (; j < E; ++j) rank += (lw[j] > ve) || (lw[j] == ve && j < e);
+    if (rank < top_k) {
+      s_id[w][rank] = e;
+      s_p[w][rank] = __expf(ve - m) / s;
     }
   }
-  float tot = wave_sum(lane < top_k ? my_p : 0.f);
+  __builtin_amdgcn_wave_barrier();
   if (lane < top_k) {
-    topk_ids[(size_t)t * top_k + lane] = my_id;
-    topk_weights[(size_t)t * top_k + lane] = renormalize ? my_p / tot : my_p;
+    const float p = s_p[w][lane];
+    float tot = 0.f;
+    for (int j = 0; j < top_k; ++j) tot += s_p[w][j];
+    topk_ids[(size_t)t * top_k + lane] = s_id[w][lane];
+    topk_weights[(size_t)t * top_k + lane] = renormalize ? p / tot : p;
   }
 }
 
@@ -153,10 +173,19 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, s
 
 namespace moe_host {
 
+// Small batches split K over the waves (more workgroups read W_r at once).
+constexpr int kSplitKMaxTokens = 256;
+
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
-  dim3 grid(ceil_div_host(a.M, kTokTile), ceil_div_host(a.E, kExpTile));
-  hipLaunchKernelGGL(route_logits_kernel, grid, dim3(256), 0, s, a.x, a.w_router, a.bias, a.M,
-                     a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
+  if (a.M <= kSplitKMaxTokens) {
+    dim3 grid(ceil_div_host(a.M, kTokTile), ceil_div_host(a.E, 16));
+    hipLaunchKernelGGL(route_logits_kernel<true>, grid, dim3(256), 0, s, a.x, a.w_router,
+                       a.bias, a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
+  } else {
+    dim3 grid(ceil_div_host(a.M, kTokTile), ceil_div_host(a.E, 64));
+    hipLaunchKernelGGL(route_logits_kernel<false>, grid, dim3(256), 0, s, a.x, a.w_router,
+                       a.bias, a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
+  }
   return hipGetLastError();
 }
 

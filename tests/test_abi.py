@@ -111,10 +111,14 @@ def test_other_calls_argument_checks():
     fake = ctypes.c_void_p(0x10000)
     info = moe.DispatchInfo()
     # align: block_m out of range, null outputs, M = 0
-    assert lib.moe_align(fake, 4, 2, 8, 0, fake, fake, fake, NULL, NULL) == -2
-    assert lib.moe_align(fake, 4, 2, 8, 300, fake, fake, fake, NULL, NULL) == -2
-    assert lib.moe_align(fake, 4, 2, 8, 16, NULL, fake, fake, NULL, NULL) == -1
-    assert lib.moe_align(fake, 0, 2, 8, 16, NULL, NULL, NULL, NULL, NULL) == 0
+    assert lib.moe_align(fake, 4, 2, 8, 0, fake, fake, fake, NULL, NULL, 0, NULL) == -2
+    assert lib.moe_align(fake, 4, 2, 8, 300, fake, fake, fake, NULL, NULL, 0, NULL) == -2
+    assert lib.moe_align(fake, 4, 2, 8, 16, NULL, fake, fake, NULL, NULL, 0, NULL) == -1
+    assert lib.moe_align(fake, 0, 2, 8, 16, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 0
+    # large batches need align scratch; small ones need none
+    assert moe.moe_align_workspace_size(4, 2, 8) == 0
+    assert moe.moe_align_workspace_size(8192, 8, 256) > 0
+    assert lib.moe_align(fake, 8192, 8, 256, 16, fake, fake, fake, NULL, NULL, 0, NULL) == -3
     # GEMMs: block_m must be 16, 64 or 128
     assert lib.moe_grouped_gemm_w13_act(fake, fake, fake, fake, fake, 4, 2, 8, 64, 32, 32,
                                         fake, ctypes.byref(info), NULL) == -2
