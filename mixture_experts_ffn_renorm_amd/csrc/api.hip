@@ -23,11 +23,10 @@ long long sorted_capacity(long long P, int E, int B) {
 }
 
 // Workspace regions of moe_forward for one (M, E, top_k, H, I, block_m).
-// The fp32 per-token sums and the arrival counters are adjacent so that one
-// pass clears both.
+// Only the combine arrival counters need clearing before GEMM 2.
 struct Layout {
-  size_t ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, acc, cnt, total;
-  size_t zero_words;  // 4-byte words of acc + cnt
+  size_t ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, partial, cnt, total;
+  size_t zero_words;  // 4-byte words of cnt
 };
 
 Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
@@ -39,12 +38,10 @@ Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
     off = align_up(off + bytes);
     return o;
   };
-  L.acc = take(0);
-  const size_t acc_bytes = (size_t)M * H * 4;
   const size_t cnt_bytes = (size_t)M * ((H + kCounterCols - 1) / kCounterCols) * 4;
-  L.cnt = L.acc + acc_bytes;
-  take(acc_bytes + cnt_bytes);
-  L.zero_words = (acc_bytes + cnt_bytes) / 4;
+  L.cnt = take(cnt_bytes);
+  L.zero_words = cnt_bytes / 4;
+  L.partial = take((size_t)P * H * 4);
   L.ids = take((size_t)P * 4);
   L.wts = take((size_t)P * 4);
   L.logits = take((size_t)M * E * 4);
@@ -219,11 +216,11 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
       !expert_block_offsets || !out)
     return MOE_ERR_INVALID_ARG;
   const Layout L = forward_layout(M, E, top_k, H, I, block_m);
-  const size_t need = L.zero_words * 4;
+  const size_t need = L.partial + (size_t)M * top_k * H * 4;
   if (workspace == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  MOE_TRY_HIP(launch_fill_zero(reinterpret_cast<float*>(ws + L.acc), L.zero_words, s));
+  MOE_TRY_HIP(launch_fill_zero(reinterpret_cast<float*>(ws + L.cnt), L.zero_words, s));
   GemmArgs g = gemm_args(M, top_k, E, H, I, block_m);
   g.a_src = act;
   g.w = w2;
@@ -232,7 +229,7 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
   g.expert_ids = expert_ids;
   g.expert_block_offsets = expert_block_offsets;
   g.out = out;
-  g.acc = reinterpret_cast<float*>(ws + L.acc);
+  g.partial = reinterpret_cast<float*>(ws + L.partial);
   g.counters = reinterpret_cast<int32_t*>(ws + L.cnt);
   return run_gemm2(g, s);
 }
@@ -261,7 +258,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
 
   RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
                reinterpret_cast<float*>(ws + L.logits), ids, wts,
-               reinterpret_cast<float*>(ws + L.acc), L.zero_words};
+               reinterpret_cast<float*>(ws + L.cnt), L.zero_words};
   MOE_TRY_HIP(launch_route_logits(ra, s));
   MOE_TRY_HIP(launch_route_topk(ra, s));
   AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
@@ -281,7 +278,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   g.w = w2;
   g.topk_weights = wts;
   g.out = out;
-  g.acc = reinterpret_cast<float*>(ws + L.acc);
+  g.partial = reinterpret_cast<float*>(ws + L.partial);
   g.counters = reinterpret_cast<int32_t*>(ws + L.cnt);
   return run_gemm2(g, s);
 }

@@ -20,10 +20,11 @@
 //   partial tiles through LDS; wave 0 applies SiLU(gate) * up and writes
 //   act rows p (pair order).
 // GEMM 2: a workgroup owns 64 rows of W2[e] (16 per wave, full K); the
-//   epilogue scales by topk_weights[p], adds into the fp32 per-token sums,
-//   and the last of the top_k contributions to a (token, 64 columns) piece
-//   writes it as bf16 (page sections "Put the results back, and combine
-//   them per token" and "The rest of the layer stays in pair order").
+//   epilogue scales by topk_weights[p] and stores fp32 partial row p; the
+//   last of the top_k workgroups producing a (token, 64 columns) piece adds
+//   the token's partial rows in slot order and writes it as bf16 (page
+//   sections "Put the results back, and combine them per token" and "The
+//   rest of the layer stays in pair order").
 #include "moe_common.h"
 
 using namespace moe;
@@ -96,9 +97,12 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_weights, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ boff, int M,
-    int top_k, int E, int H, int I, uint16_t* __restrict__ out, float* __restrict__ accum,
+    int top_k, int E, int H, int I, uint16_t* __restrict__ out, float* __restrict__ partial,
     int32_t* __restrict__ counters) {
   __shared__ int s_last[kBM];
+  __shared__ int s_pair[kBM];
+  __shared__ float s_wt[kBM];
+  __shared__ float ct[kBM][65];
   const int b = blockIdx.x;
   if (b >= boff[E]) return;
   const int P = M * top_k;
@@ -128,25 +132,41 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(
     for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(wa[s], ab[s], acc);
   }
 
-  // lane holds output columns blockIdx.y*64 + wv*16 + 4g + q of pair r
-  const int hf = blockIdx.y * 64 + wv * 16 + 4 * g;
-  if (p_ok && hf < H) {
-    const int t = p / top_k;
-    const float wt = topk_weights[p];
-    float* dst = accum + (size_t)t * H + hf;
+  // lane holds output columns blockIdx.y*64 + wv*16 + 4g + q of pair r.
+  // The workgroup's 64-column x 16-pair tile goes through LDS so that each
+  // store instruction writes 64 consecutive columns of one partial row
+  // (row p = topk_weights[p] * (W2[e] act[p]), fp32, agent-coherent stores).
+  ct[r][wv * 16 + 4 * g + 0] = acc[0];
+  ct[r][wv * 16 + 4 * g + 1] = acc[1];
+  ct[r][wv * 16 + 4 * g + 2] = acc[2];
+  ct[r][wv * 16 + 4 * g + 3] = acc[3];
+  if (threadIdx.x < kBM) {
+    const int pp = sorted[b * kBM + threadIdx.x];
+    s_pair[threadIdx.x] = pp;
+    s_wt[threadIdx.x] = pp < P ? topk_weights[pp] : 0.f;
+  }
+  __syncthreads();
+  const int hc = blockIdx.y * 64 + lane;
+  if (hc < H) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) unsafeAtomicAdd(dst + q, wt * acc[q]);
+    for (int i = 0; i < 4; ++i) {
+      const int pr = wv * 4 + i;
+      const int pp = s_pair[pr];
+      if (pp >= P) continue;
+      __hip_atomic_store(partial + (size_t)pp * H + hc, s_wt[pr] * ct[pr][lane], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
-  // Every wave waits until its additions are performed, then the workgroup
+  // Every wave waits until its stores have completed, then the workgroup
   // counts one arrival per (token, 64 columns).  The last of the top_k
-  // arrivals reads the finished sums with atomic exchanges (served where
-  // the additions were performed; they also leave the sums at zero).
+  // arrivals adds the token's top_k partial rows in slot order (coherent
+  // loads) and writes the bf16 output piece.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int ncg = ceil_div(H, 64);
   if (threadIdx.x < kBM) {
-    const int pr = sorted[b * kBM + threadIdx.x];
+    const int pr = s_pair[threadIdx.x];
     int last = -1;
     if (pr < P) {
       const int t = pr / top_k;
@@ -159,11 +179,9 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(
   for (int it = wv; it < kBM; it += 4) {
     const int t = s_last[it];
     if (t < 0) continue;
-    const int col = blockIdx.y * 64 + lane;
-    if (col < H) {
-      const float v = atomicExch(accum + (size_t)t * H + col, 0.0f);
-      out[(size_t)t * H + col] = (uint16_t)f32_to_bf16(v);
-    }
+    if (hc < H)
+      out[(size_t)t * H + hc] =
+          (uint16_t)f32_to_bf16(sum_partials(partial + (size_t)t * top_k * H + hc, H, top_k));
   }
 }
 
@@ -183,7 +201,7 @@ hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s) {
   dim3 grid(a.max_blocks, ceil_div_host(a.H, 64));
   hipLaunchKernelGGL(gemm2_stream_kernel, grid, dim3(256), 0, s, a.a_src, a.w, a.topk_weights,
                      a.sorted_token_ids, a.expert_ids, a.expert_block_offsets, a.M, a.top_k,
-                     a.E, a.H, a.I, a.out, a.acc, a.counters);
+                     a.E, a.H, a.I, a.out, a.partial, a.counters);
   return hipGetLastError();
 }
 

@@ -2,40 +2,81 @@
 //
 // GEMM 1 (page "Mixture of Experts in vLLM - From First Principles to
 // fused_moe", sub-section "One GEMM 1 program, step by step"): a workgroup
-// owns one block of BM pairs (one expert, from the index lists) and 64
-// columns of the activation.  It reads expert_ids[b], masks pad entries
+// owns one block of BM pairs (one expert, from the index lists) and 128
+// columns of the activation.  It reads expert_ids[b], skips pad entries
 // (id >= M*top_k), reads input row p // top_k of x in place, multiplies by
-// the matching 64 gate rows and 64 up rows of W13[e], and writes
+// the matching 128 gate rows and 128 up rows of W13[e], and writes
 // SiLU(gate) * up to row p of act (sub-section "The rest of the layer stays
 // in pair order"), so the [M*top_k, 2I] product never reaches memory.
 //
 // GEMM 2 (same page, "The rest of the layer stays in pair order" and "Put
 // the results back, and combine them per token"): the same tiling over
-// act (row p read directly) and W2[e]; the epilogue scales row p by
-// topk_weights[p] and adds it into an fp32 per-token sum; the last of the
-// top_k contributions to a (token, 64-column group) converts that group to
-// bf16 in token order, so the [M*top_k, H] product never reaches memory.
+// act (row p read directly) and 256 rows of W2[e]; the epilogue scales row p
+// by topk_weights[p] and stores it as an fp32 partial row p; the last of the
+// top_k workgroups that produce a (token, 64-column group) adds that
+// token's top_k partial rows in slot order and writes the bf16 output row
+// piece in token order (no separate sum kernel, no atomic adds on data).
 //
-// Tile: 128 weight rows x BM pairs x 64 k, 4 waves in a 2 x 2 layout, each
-// wave 64 weight rows x BM/2 pairs of 16x16x32 bf16 MFMAs.  Operands are
-// staged through double-buffered LDS with a 16-byte row pad (row stride
-// 144 B keeps the 16 rows of one MFMA operand read on distinct banks).
+// Tile: 256 weight rows x BM pairs x 64 k per stage, 8 waves in a 4 x 2
+// layout, each wave 64 weight rows x BM/2 pairs of 16x16x32 bf16 MFMAs.
 // Weights are the MFMA A operand and pairs the B operand, so each lane ends
-// with 4 consecutive features of one pair (8-byte bf16 stores for act).
+// with 4 consecutive features of one pair.
+//
+// Memory pipeline: operands go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register staging), three stages deep.  One
+// load instruction of a wave fills 1 KB of LDS = 8 rows of 64 k values; a
+// row's eight 16-byte chunks are stored XOR-swizzled (chunk c of row R at
+// slot c ^ ((R >> 1) & 7)), so the 16 rows that one MFMA operand read
+// touches fall on distinct banks, while each global access still reads
+// whole 128-byte row pieces.  Rows or k ranges outside the operands (pads,
+// features past the end, the K tail) load from a zeroed 16-byte page.
 #include "moe_common.h"
 
 using namespace moe;
 
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kLdsStride = kBK + 8;   // elements per LDS row
-constexpr int kWRows = 128;           // weight rows per tile
-constexpr int kThreads = 256;
+constexpr int kBK = 64;          // k elements per stage = 128 bytes per row
+constexpr int kBN = 256;         // weight rows per tile
+constexpr int kStages = 3;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowBytes = kBK * 2;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// 16 zero bytes that out-of-range lanes load instead of real data.
+__device__ __attribute__((aligned(16))) const uint32_t kZeroPage[4] = {0u, 0u, 0u, 0u};
 
 template <int BM>
-constexpr size_t lds_bytes() {
-  return (size_t)2 * (kWRows + BM) * kLdsStride * sizeof(uint16_t);
+struct TileCfg {
+  static constexpr int kWGroups = kBN / 8 / kWaves;   // 8-row W groups per wave (4)
+  static constexpr int kXGroups = BM / 8 / kWaves;    // 8-row X groups per wave (2 or 1)
+  static constexpr int kLoads = kWGroups + kXGroups;  // load instructions per stage
+  static constexpr int kStageBytes = (kBN + BM) * kRowBytes;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kNT = BM / 32;                 // 16-pair MFMA tiles per wave
+};
+
+// Slot of a row's 16-byte chunk: chunk c of row R sits at c ^ swz(R).  With
+// this choice the 16 rows read by one MFMA operand load (same chunk, rows
+// R0..R0+15) hit distinct LDS banks on gfx950 (measured: the same
+// ds_read_b128 throughput as contiguous reads; a 144-byte padded row
+// stride, or the XOR with (R ^ (R >> 3)) & 7, both run at about half).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ void load_lds16(const void* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+
+// Waits until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  // gfx9 s_waitcnt encoding: vmcnt = bits 3:0 and 15:14; expcnt (6:4) and
+  // lgkmcnt (11:8) left at their maxima, i.e. not waited on.
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 struct TileParams {
@@ -48,17 +89,18 @@ struct TileParams {
   int M, top_k, E, H, I;
   int ntiles_n;        // feature tiles per block
   uint16_t* out;
-  float* acc;
+  float* partial;      // GEMM 2: [M*top_k, H] fp32 weighted partial rows
   int32_t* counters;
 };
 
 template <int BM, bool kGemm1>
-__global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  constexpr int NT = BM / 32;                // 16-pair tiles per wave
-  constexpr int XR = BM / 32;                // pair rows loaded per thread
-  uint16_t* Ws = lds;                                   // [2][128][72]
-  uint16_t* Xs = lds + 2 * kWRows * kLdsStride;         // [2][BM][72]
+__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(TileParams prm) {
+  using C = TileCfg<BM>;
+  constexpr int NT = C::kNT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int s_pair[BM];
+  __shared__ float s_wt[BM];
+  __shared__ int s_last[4 * BM];
 
   const int P = prm.M * prm.top_k;
   const int nblocks = prm.boff[prm.E];
@@ -69,67 +111,92 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm)
   const int e = prm.expert_ids[b];
   const int K = kGemm1 ? prm.H : prm.I;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wf = wv & 1, wp = wv >> 1;
 
-  // ---- per-thread global row pointers (chunk c of rows rg + 32 i) ----
-  const int c = tid & 7, rg = tid >> 3;
-  const uint16_t* wptr[4];
-  const uint16_t* xptr[XR];
+  if (tid < BM) {
+    const int p = prm.sorted[b * BM + tid];
+    s_pair[tid] = p;
+    s_wt[tid] = (!kGemm1 && p < P) ? prm.topk_weights[p] : 0.f;
+  }
+
+  // ---- per-lane source row of each load slot (row R of the LDS tile) ----
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const uint16_t* wsrc[C::kWGroups];
+  int wchunk[C::kWGroups];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = rg + 32 * i;
+  for (int i = 0; i < C::kWGroups; ++i) {
+    const int R = (wv + kWaves * i) * 8 + lrow;
+    wchunk[i] = lpos ^ swz(R);
+    const uint16_t* row = nullptr;
     if (kGemm1) {
-      const int n0 = nt * 64;
-      const int f = r < 64 ? n0 + r : n0 + (r - 64);
-      const bool ok = f < prm.I;
-      const size_t row = (size_t)e * 2 * prm.I + (r < 64 ? f : prm.I + f);
-      wptr[i] = ok ? prm.w + row * K : nullptr;
+      const int f = nt * 128 + (R & 127);
+      if (f < prm.I)
+        row = prm.w + ((size_t)e * 2 * prm.I + (R < 128 ? f : prm.I + f)) * K;
     } else {
-      const int h = nt * 128 + r;
-      wptr[i] = h < prm.H ? prm.w + ((size_t)e * prm.H + h) * K : nullptr;
+      const int h = nt * kBN + R;
+      if (h < prm.H) row = prm.w + ((size_t)e * prm.H + h) * K;
     }
+    wsrc[i] = row;
   }
+  const uint16_t* xsrc[C::kXGroups];
+  int xchunk[C::kXGroups];
 #pragma unroll
-  for (int i = 0; i < XR; ++i) {
-    const int p = prm.sorted[b * BM + rg + 32 * i];
+  for (int i = 0; i < C::kXGroups; ++i) {
+    const int R = (wv + kWaves * i) * 8 + lrow;
+    xchunk[i] = lpos ^ swz(R);
+    const int p = prm.sorted[b * BM + R];
+    const uint16_t* row = nullptr;
     if (p < P)
-      xptr[i] = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * prm.H
-                       : prm.a_src + (size_t)p * prm.I;
-    else
-      xptr[i] = nullptr;
+      row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * prm.H
+                   : prm.a_src + (size_t)p * prm.I;
+    xsrc[i] = row;
   }
 
-  u32x4 wreg[4], xreg[XR];
-  auto gload = [&](int kt) {
-    const int k = kt * kBK + c * 8;
-    const bool kin = k < K;
+  auto issue_stage = [&](int kt, int buf) {
+    uint8_t* sb = lds + buf * C::kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wreg[i] = load16_or_zero(wptr[i] + k, wptr[i] != nullptr && kin);
+    for (int i = 0; i < C::kWGroups; ++i) {
+      const int k = kt * kBK + wchunk[i] * 8;
+      const void* src = (wsrc[i] != nullptr && k < K) ? (const void*)(wsrc[i] + k)
+                                                      : (const void*)kZeroPage;
+      load_lds16(src, sb + (wv + kWaves * i) * 8 * kRowBytes);
+    }
 #pragma unroll
-    for (int i = 0; i < XR; ++i) xreg[i] = load16_or_zero(xptr[i] + k, xptr[i] != nullptr && kin);
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* wb = Ws + buf * kWRows * kLdsStride;
-    uint16_t* xb = Xs + buf * BM * kLdsStride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(wb + (rg + 32 * i) * kLdsStride + c * 8) = wreg[i];
-#pragma unroll
-    for (int i = 0; i < XR; ++i)
-      *reinterpret_cast<u32x4*>(xb + (rg + 32 * i) * kLdsStride + c * 8) = xreg[i];
+    for (int i = 0; i < C::kXGroups; ++i) {
+      const int k = kt * kBK + xchunk[i] * 8;
+      const void* src = (xsrc[i] != nullptr && k < K) ? (const void*)(xsrc[i] + k)
+                                                      : (const void*)kZeroPage;
+      load_lds16(src, sb + (kBN + (wv + kWaves * i) * 8) * kRowBytes);
+    }
   };
 
-  // A tiles (weight rows in the LDS tile) of this wave
+  // ---- this wave's MFMA tiles ----
+  const int wf = wv & 3, wp = wv >> 2;
   int arow[4];
   if (kGemm1) {
-    arow[0] = wf * 32;       arow[1] = wf * 32 + 16;        // gate
-    arow[2] = 64 + wf * 32;  arow[3] = 64 + wf * 32 + 16;   // matching up rows
+    arow[0] = wf * 32;        arow[1] = wf * 32 + 16;         // gate rows
+    arow[2] = 128 + wf * 32;  arow[3] = 128 + wf * 32 + 16;   // matching up rows
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) arow[i] = wf * 64 + 16 * i;
   }
   const int brow0 = wp * (BM / 2);
   const int r16 = lane & 15, kg = lane >> 4;
+  // byte offsets inside a stage of this lane's operand reads, per k half s
+  int aoff[2][4], boffs[2][NT];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c = s * 4 + kg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int R = arow[i] + r16;
+      aoff[s][i] = R * kRowBytes + ((c ^ swz(R)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int R = brow0 + 16 * j + r16;
+      boffs[s][j] = (kBN + R) * kRowBytes + ((c ^ swz(R)) << 4);
+    }
+  }
 
   f32x4 acc[4][NT];
 #pragma unroll
@@ -138,31 +205,32 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm)
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = ceil_div(K, kBK);
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  issue_stage(0, 0);
+  if (nk > 1) issue_stage(1, 1);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* wb = Ws + cur * kWRows * kLdsStride;
-    const uint16_t* xb = Xs + cur * BM * kLdsStride;
+    // stage kt has landed once at most the next stage's loads are pending
+    if (kt + 1 < nk) wait_vmem<C::kLoads>(); else wait_vmem<0>();
+    // Every wave's part of stage kt is in LDS, and stage kt-1 is consumed.
+    // A plain barrier: a fenced one would also wait for the stages still in
+    // flight.  The empty asm statements keep the compiler from moving LDS
+    // accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) issue_stage(kt + 2, (kt + 2) % kStages);
+    const uint8_t* sb = lds + (kt % kStages) * C::kStageBytes;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int kof = s * 32 + kg * 8;
       u32x4 af[4], bfr[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(wb + (arow[i] + r16) * kLdsStride + kof);
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + aoff[s][i]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4*>(xb + (brow0 + 16 * j + r16) * kLdsStride + kof);
+      for (int j = 0; j < NT; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(sb + boffs[s][j]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogues: lane holds features 4*kg + q of each A tile, pair r16 of each B tile ----
@@ -170,11 +238,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm)
     const int I = prm.I;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int p = prm.sorted[b * BM + brow0 + 16 * j + r16];
+      const int p = s_pair[brow0 + 16 * j + r16];
       if (p >= P) continue;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int n = nt * 64 + wf * 32 + 16 * i + 4 * kg;
+        const int n = nt * 128 + wf * 32 + 16 * i + 4 * kg;
         if (n >= I) continue;
         const f32x4 gt = acc[i][j], up = acc[i + 2][j];
         u32x2 v;
@@ -186,55 +254,66 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(TileParams prm)
     return;
   }
 
+  // GEMM 2: the wave's 64 x BM/2 tile goes through LDS so that each store
+  // instruction writes 64 consecutive columns of one partial row.  Row p of
+  // the fp32 partials holds topk_weights[p] * (W2[e] act[p]); the stores are
+  // agent-coherent, so other workgroups' coherent loads see them once they
+  // have completed.
   const int H = prm.H;
+  constexpr int kCt = 65;                           // row stride in floats
+  __syncthreads();                                  // all waves done reading the stages
+  float* ct = reinterpret_cast<float*>(lds) + wv * (BM / 2) * kCt;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int p = prm.sorted[b * BM + brow0 + 16 * j + r16];
-    if (p >= P) continue;
-    const int t = p / prm.top_k;
-    const float wt = prm.topk_weights[p];
-    float* dst = prm.acc + (size_t)t * H;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = nt * 128 + wf * 64 + 16 * i + 4 * kg;
-      if (h >= H) continue;
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) unsafeAtomicAdd(dst + h + q, wt * acc[i][j][q]);
+      for (int q = 0; q < 4; ++q) ct[(16 * j + r16) * kCt + 16 * i + 4 * kg + q] = acc[i][j][q];
+  __builtin_amdgcn_wave_barrier();
+  const int h = nt * kBN + wf * 64 + lane;
+  if (h < H) {
+    for (int pr = 0; pr < BM / 2; ++pr) {
+      const int p = s_pair[brow0 + pr];
+      if (p >= P) continue;
+      __hip_atomic_store(prm.partial + (size_t)p * H + h, s_wt[brow0 + pr] * ct[pr * kCt + lane],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  // ---- last arrival per (token, 64-column group) writes the bf16 row piece.
-  // Every wave waits until its additions are performed, then the workgroup
-  // counts its arrivals; the last of the top_k arrivals reads the finished
-  // sums with atomic exchanges (served where the additions were performed;
-  // they also leave the sums at zero).
-  __shared__ int s_last[2 * BM];
+  // The last arrival per (token, 64-column group) sums the token's top_k
+  // partial rows in slot order and writes the bf16 result.  Every wave first
+  // waits until its own stores have completed; the workgroup then counts
+  // its arrivals (4 column groups per tile).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int ncg = ceil_div(H, 64);
-  if (tid < 2 * BM) {
-    const int r = tid % BM, cgl = tid / BM;
-    const int cg = nt * 2 + cgl;
-    const int p = prm.sorted[b * BM + r];
+  for (int it = tid; it < 4 * BM; it += kThreads) {
+    const int r = it % BM, cgl = it / BM;
+    const int cg = nt * 4 + cgl;
+    const int p = s_pair[r];
     int last = -1;
     if (p < P && cg < ncg) {
       const int t = p / prm.top_k;
       const int old = atomicAdd(prm.counters + (size_t)t * ncg + cg, 1);
       if (old == prm.top_k - 1) last = t;
     }
-    s_last[tid] = last;
+    s_last[it] = last;
   }
   __syncthreads();
-  for (int it = wv; it < 2 * BM; it += 4) {
+  for (int it = wv; it < 4 * BM; it += kWaves) {
     const int t = s_last[it];
     if (t < 0) continue;
-    const int col = (nt * 2 + it / BM) * 64 + lane;
-    if (col < H) {
-      const float v = atomicExch(prm.acc + (size_t)t * H + col, 0.0f);
-      prm.out[(size_t)t * H + col] = (uint16_t)f32_to_bf16(v);
-    }
+    const int col = (nt * 4 + it / BM) * 64 + lane;
+    if (col < H)
+      prm.out[(size_t)t * H + col] =
+          (uint16_t)f32_to_bf16(sum_partials(prm.partial + (size_t)t * prm.top_k * H + col, H,
+                                             prm.top_k));
   }
 }
+
+// the GEMM 2 epilogue reuses the stage LDS for 8 waves x (BM/2) x 65 floats
+static_assert(TileCfg<64>::kLdsBytes >= kWaves * 32 * 65 * 4, "epilogue LDS");
+static_assert(TileCfg<128>::kLdsBytes >= kWaves * 64 * 65 * 4, "epilogue LDS");
 
 template <int BM, bool kGemm1>
 hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s) {
@@ -250,13 +329,13 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s) {
   prm.E = a.E;
   prm.H = a.H;
   prm.I = a.I;
-  prm.ntiles_n = kGemm1 ? moe_host::ceil_div_host(a.I, 64) : moe_host::ceil_div_host(a.H, 128);
+  prm.ntiles_n = kGemm1 ? moe_host::ceil_div_host(a.I, 128) : moe_host::ceil_div_host(a.H, kBN);
   prm.out = a.out;
-  prm.acc = a.acc;
+  prm.partial = a.partial;
   prm.counters = a.counters;
   const long long tiles = (long long)a.max_blocks * prm.ntiles_n;
   const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-  const size_t lds = lds_bytes<BM>();
+  const size_t lds = TileCfg<BM>::kLdsBytes;
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(

@@ -73,6 +73,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum of the top_k fp32 partial rows of one token at one column, in slot
+// order, read with agent-coherent loads (rows written by other workgroups).
+// All loads are issued before the first add.
+__device__ __forceinline__ float sum_partials(const float* src, int stride, int top_k) {
+  constexpr int kMaxK = 32;
+  float v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < top_k)
+      v[j] = __hip_atomic_load(src + (size_t)j * stride, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < top_k) sum += v[j];
+  return sum;
+}
+
 // Workgroups are handed to the 8 XCDs of the chip round-robin (id % 8).
 // Map a linear workgroup id to a logical tile id so that every XCD works on
 // one contiguous range of logical tiles (tiles that share operands then
@@ -100,7 +118,7 @@ struct RouteArgs {
   float* logits;        // [M, E] scratch or caller output
   int32_t* topk_ids;    // [M, top_k]
   float* topk_weights;  // [M, top_k]
-  float* zero_ptr;      // optional region to clear (fp32 sums + counters)
+  float* zero_ptr;      // optional region to clear (combine arrival counters)
   size_t zero_words;    // number of 4-byte words to clear
 };
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s);
@@ -130,8 +148,8 @@ struct GemmArgs {
   const float* topk_weights; // GEMM 2 only
   int M, top_k, E, H, I, block_m, max_blocks;
   uint16_t* out;             // GEMM 1: act [P, I]; GEMM 2: out [M, H]
-  float* acc;                // GEMM 2: fp32 per-token sums [M, H] (zeroed)
-  int32_t* counters;         // GEMM 2: arrival counters (zeroed)
+  float* partial;            // GEMM 2: fp32 weighted partial rows [P, H]
+  int32_t* counters;         // GEMM 2: arrival counters [M, ceil(H/64)] (zeroed)
 };
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
@@ -141,8 +159,8 @@ hipError_t launch_fill_zero(float* p, size_t words, hipStream_t s);
 
 // Tile constants the host needs for grids and counters.
 constexpr int kTiledBK = 64;
-constexpr int kTiledG1Features = 64;    // act columns per GEMM 1 tile (64 gate + 64 up rows)
-constexpr int kTiledG2Features = 128;   // output columns per GEMM 2 tile
+constexpr int kTiledG1Features = 128;   // act columns per GEMM 1 tile (128 gate + 128 up rows)
+constexpr int kTiledG2Features = 256;   // output columns per GEMM 2 tile
 constexpr int kStreamG1Features = 16;   // act columns per streaming GEMM 1 workgroup
 constexpr int kStreamG2Features = 64;   // output columns per streaming GEMM 2 workgroup
 constexpr int kStreamBK = 256;          // K elements per streaming super-chunk

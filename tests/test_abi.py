@@ -65,10 +65,11 @@ def test_workspace_size_monotone_and_bounded():
         n = moe.moe_workspace_size(M, 256, 8, 2048, 512)
         assert n >= prev
         prev = n
-    # act [P, I] bf16 + fp32 sums [M, H] dominate: about 135 MB at M = 8192
+    # act [P, I] bf16 + fp32 partial rows [P, H] dominate: ~604 MB at M = 8192
     n = moe.moe_workspace_size(8192, 256, 8, 2048, 512)
     P = 8192 * 8
-    assert P * 512 * 2 + 8192 * 2048 * 4 <= n <= 1.2 * (P * 512 * 2 + 8192 * 2048 * 4) + (8 << 20)
+    big = P * 512 * 2 + P * 2048 * 4
+    assert big <= n <= 1.05 * big + (16 << 20)
     assert moe.moe_workspace_size(1, 600, 8, 2048, 512) == 0     # E > 512
     assert moe.moe_workspace_size(1, 128, 8, 2044, 512) == 0     # H % 8 != 0
 
