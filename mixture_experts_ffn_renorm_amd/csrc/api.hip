@@ -106,6 +106,24 @@ int run_gemm2(GemmArgs g, hipStream_t s) {
 
 }  // namespace
 
+namespace moe_host {
+
+int device_cu_count() {
+  static int cached[64] = {0};   // benign race: every writer stores the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace moe_host
+
 extern "C" {
 
 size_t moe_workspace_size(int M_max, int E, int top_k, int H, int I) {

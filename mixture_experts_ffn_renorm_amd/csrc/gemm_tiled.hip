@@ -43,12 +43,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowBytes = kBK * 2;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef const __attribute__((address_space(1))) void gbl_void_t;
-
-// 16 zero bytes that out-of-range lanes load instead of real data.
-__device__ __attribute__((aligned(16))) const uint32_t kZeroPage[4] = {0u, 0u, 0u, 0u};
-
 template <int BM>
 struct TileCfg {
   static constexpr int kWGroups = kBN / 8 / kWaves;   // 8-row W groups per wave (4)
@@ -65,19 +59,6 @@ struct TileCfg {
 // ds_read_b128 throughput as contiguous reads; a 144-byte padded row
 // stride, or the XOR with (R ^ (R >> 3)) & 7, both run at about half).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-__device__ __forceinline__ void load_lds16(const void* src, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
-}
-
-// Waits until at most N vector-memory operations of this wave are pending.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  // gfx9 s_waitcnt encoding: vmcnt = bits 3:0 and 15:14; expcnt (6:4) and
-  // lgkmcnt (11:8) left at their maxima, i.e. not waited on.
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 struct TileParams {
   const uint16_t* a_src;
@@ -211,12 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(TileParams prm)
     // stage kt has landed once at most the next stage's loads are pending
     if (kt + 1 < nk) wait_vmem<C::kLoads>(); else wait_vmem<0>();
     // Every wave's part of stage kt is in LDS, and stage kt-1 is consumed.
-    // A plain barrier: a fenced one would also wait for the stages still in
-    // flight.  The empty asm statements keep the compiler from moving LDS
-    // accesses across it.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    barrier_nofence();
     if (kt + 2 < nk) issue_stage(kt + 2, (kt + 2) % kStages);
     const uint8_t* sb = lds + (kt % kStages) * C::kStageBytes;
 #pragma unroll

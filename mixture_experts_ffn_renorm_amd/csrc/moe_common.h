@@ -61,6 +61,41 @@ __device__ __forceinline__ u32x4 load16_or_zero(const void* p, bool ok) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// ---- global -> LDS copies (global_load_lds_dwordx4) ----
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// 16 zero bytes that out-of-range lanes copy instead of real data.
+static __device__ __attribute__((aligned(16))) const uint32_t kZeroPage[4] = {0u, 0u, 0u, 0u};
+
+// Cache policy of a copy: 0 = default, kNonTemporal = streamed once.
+constexpr int kNonTemporal = 2;
+
+// Each lane copies 16 bytes from `src` to LDS at lds_dst + 16 * lane
+// (lds_dst must be the same for the whole wave).
+template <int kPolicy = 0>
+__device__ __forceinline__ void load_lds16(const void* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 16, 0, kPolicy);
+}
+
+// Waits until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  // gfx9 s_waitcnt encoding: vmcnt = bits 3:0 and 15:14; expcnt (6:4) and
+  // lgkmcnt (11:8) left at their maxima, i.e. not waited on.
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence (a fenced barrier also waits for
+// every copy still in flight).  The empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wave-wide reductions over 64 lanes.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -161,9 +196,12 @@ hipError_t launch_fill_zero(float* p, size_t words, hipStream_t s);
 constexpr int kTiledBK = 64;
 constexpr int kTiledG1Features = 128;   // act columns per GEMM 1 tile (128 gate + 128 up rows)
 constexpr int kTiledG2Features = 256;   // output columns per GEMM 2 tile
-constexpr int kStreamG1Features = 16;   // act columns per streaming GEMM 1 workgroup
-constexpr int kStreamG2Features = 64;   // output columns per streaming GEMM 2 workgroup
-constexpr int kStreamBK = 256;          // K elements per streaming super-chunk
-constexpr int kCounterCols = 64;        // combine counters: one per (token, 64 columns)
+constexpr int kStreamG1Features = 16;   // act columns per streaming GEMM 1 tile
+constexpr int kStreamG2Features = 32;   // output columns per streaming GEMM 2 tile
+constexpr int kStreamBK = 256;          // K elements per streaming LDS slice
+constexpr int kCounterCols = 32;        // combine counters: room for one per (token, 32 columns)
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 }  // namespace moe_host
