@@ -66,6 +66,10 @@ int check_sizes(int M, int E, int top_k, int H, int I) {
 
 bool gemm_block_ok(int B) { return B == 16 || B == 64 || B == 128; }
 
+// Kernels queued by one GEMM 2 call: streaming = GEMM 2 + per-token sum;
+// tiled = counter clearing (standalone call only) + GEMM 2 with the fused sum.
+int gemm2_launches(int B, bool standalone) { return B == 16 ? 2 : (standalone ? 2 : 1); }
+
 void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches) {
   if (info == nullptr) return;
   const bool stream = B == 16;
@@ -228,7 +232,7 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
   int st = check_sizes(M, E, top_k, H, I);
   if (st != MOE_OK) return st;
   if (!gemm_block_ok(block_m)) return MOE_ERR_UNSUPPORTED;
-  fill_info(info, block_m, H, I, M == 0 ? 0 : 2);
+  fill_info(info, block_m, H, I, M == 0 ? 0 : gemm2_launches(block_m, true));
   if (M == 0) return MOE_OK;
   if (!act || !w2 || !topk_weights || !sorted_token_ids || !expert_ids ||
       !expert_block_offsets || !out)
@@ -238,7 +242,8 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
   if (workspace == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  MOE_TRY_HIP(launch_fill_zero(reinterpret_cast<float*>(ws + L.cnt), L.zero_words, s));
+  if (block_m != 16)   // the tiled kernel's fused sum counts arrivals
+    MOE_TRY_HIP(launch_fill_zero(reinterpret_cast<float*>(ws + L.cnt), L.zero_words, s));
   GemmArgs g = gemm_args(M, top_k, E, H, I, block_m);
   g.a_src = act;
   g.w = w2;
@@ -260,7 +265,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
-  fill_info(info, B, H, I, M == 0 ? 0 : 4 + (align_segments(M * top_k) > 1 ? 2 : 1));
+  fill_info(info, B, H, I,
+            M == 0 ? 0 : 3 + (align_segments(M * top_k) > 1 ? 2 : 1) + gemm2_launches(B, false));
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
   const Layout L = forward_layout(M, E, top_k, H, I, B);
@@ -276,7 +282,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
 
   RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
                reinterpret_cast<float*>(ws + L.logits), ids, wts,
-               reinterpret_cast<float*>(ws + L.cnt), L.zero_words};
+               B == 16 ? nullptr : reinterpret_cast<float*>(ws + L.cnt),
+               B == 16 ? 0 : L.zero_words};
   MOE_TRY_HIP(launch_route_logits(ra, s));
   MOE_TRY_HIP(launch_route_topk(ra, s));
   AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
