@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
+constexpr int kTopkWaves = 4;   // tokens per workgroup of the fused top-k + align
 
 // Lanes of the wave whose (valid) id equals this lane's id.
 __device__ __forceinline__ unsigned long long match_lanes(int id, bool valid, int nbits) {
@@ -93,10 +94,10 @@ struct Seg {
   int w0, w1;   // this wave's pairs
 };
 
-__device__ __forceinline__ Seg segment(int P, int G) {
+__device__ __forceinline__ Seg segment(int P, int G, int gid) {
   Seg s;
   const int seg = ceil_div(ceil_div(P, G), 64) * 64;
-  s.s0 = min(P, (int)blockIdx.x * seg);
+  s.s0 = min(P, gid * seg);
   s.s1 = min(P, s.s0 + seg);
   const int piece = ceil_div(ceil_div(s.s1 - s.s0, kWaves), 64) * 64;
   const int w = threadIdx.x >> 6;
@@ -111,20 +112,22 @@ __global__ __launch_bounds__(kThreads) void align_count_kernel(
   extern __shared__ int hist[];   // [E]
   for (int i = threadIdx.x; i < E; i += kThreads) hist[i] = 0;
   __syncthreads();
-  const Seg sg = segment(P, G);
+  const Seg sg = segment(P, G, blockIdx.x);
   count_piece(ids, sg.w0, sg.w1, hist, id_bits(E));
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += kThreads)
     seg_counts[(size_t)blockIdx.x * E + i] = hist[i];
 }
 
-// grid G: offsets, stable scatter of this segment, block experts and pads.
-__global__ __launch_bounds__(kThreads) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int B, int G,
-    const int32_t* __restrict__ seg_counts, int32_t* __restrict__ sorted,
-    int32_t* __restrict__ expert_ids, int32_t* __restrict__ boff_out,
-    int32_t* __restrict__ counts_out) {
-  extern __shared__ int smem[];
+// Segment gid of G of the index-list build (1024 threads; smem holds
+// align_smem_ints(E) ints).  ids may live in global memory or in LDS.
+// G == 1: counts come from this workgroup's own pass; G > 1: from
+// seg_counts written by align_count_kernel.
+__device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, int B, int G, int gid,
+                              const int32_t* __restrict__ seg_counts,
+                              int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
+                              int32_t* __restrict__ boff_out, int32_t* __restrict__ counts_out,
+                              int* smem) {
   int* hist = smem;                  // [kWaves][E] counts, then running positions
   int* boff = hist + kWaves * E;     // [E + 1]
   int* cnt = boff + E + 1;           // [E]
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
 
   for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
   __syncthreads();
-  const Seg sg = segment(P, G);
+  const Seg sg = segment(P, G, gid);
   count_piece(ids, sg.w0, sg.w1, hist + w * E, nbits);
   __syncthreads();
 
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
       for (int i = 0; i < G; ++i) {
         const int c = seg_counts[(size_t)i * E + tid];
         n_e += c;
-        if (i < (int)blockIdx.x) before += c;
+        if (i < gid) before += c;
       }
     } else {
       for (int i = 0; i < kWaves; ++i) n_e += hist[i * E + tid];
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
   if (tid < E) {
     boff[tid] = excl;
     cnt[tid] = n_e;
-    if (blockIdx.x == 0) {
+    if (gid == 0) {
       boff_out[tid] = excl;
       if (counts_out != nullptr) counts_out[tid] = n_e;
     }
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
   }
   if (tid == 0) {
     boff[E] = total_blocks;
-    if (blockIdx.x == 0) boff_out[E] = total_blocks;
+    if (gid == 0) boff_out[E] = total_blocks;
   }
   __syncthreads();
 
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
   }
 
   // expert of each block and the pad entries, split over the workgroups
-  const int gtid = blockIdx.x * kThreads + tid, gstride = G * kThreads;
+  const int gtid = gid * kThreads + tid, gstride = G * kThreads;
   for (int blk = gtid; blk < total_blocks; blk += gstride)
     expert_ids[blk] = expert_of_block(boff, E, blk);
   const int nslots = total_blocks * B;
@@ -207,9 +210,89 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
   }
 }
 
+// grid G: offsets, stable scatter of this segment, block experts and pads.
+__global__ __launch_bounds__(kThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int B, int G,
+    const int32_t* __restrict__ seg_counts, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ boff_out,
+    int32_t* __restrict__ counts_out) {
+  extern __shared__ int smem[];
+  align_segment(ids, P, E, B, G, blockIdx.x, seg_counts, sorted, expert_ids, boff_out,
+                counts_out, smem);
+}
+
+// Small batches (one align segment): top-k, one wave per token on the first
+// kTopkWaves waves of each workgroup (one per SIMD, so tokens do not queue
+// behind each other), then the index lists built by the workgroup that
+// arrives last.  Each workgroup publishes its expert ids with agent-coherent
+// stores, waits for them, and counts its arrival in *arrivals (zeroed by the
+// router-logits kernel on the same stream); the last one reads all P ids
+// back with agent-coherent loads.  A lone workgroup keeps its ids in LDS.
+__global__ __launch_bounds__(kThreads) void route_topk_align_kernel(
+    const float* __restrict__ logits, int M, int E, int top_k, int renormalize, int B,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ boff_out, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ arrivals) {
+  extern __shared__ __attribute__((aligned(16))) int smem[];
+  __shared__ int s_last;
+  const int P = M * top_k;
+  int* ids_lds = smem + align_smem_ints(E);
+  float* tk = reinterpret_cast<float*>(smem + ((align_smem_ints(E) + P + 3) & ~3));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkWaves + w;
+  if (w < kTopkWaves && t < M) {
+    const TopkSlot r =
+        topk_token(logits + (size_t)t * E, E, top_k, renormalize, tk + w * topk_wave_floats(E));
+    if (lane < top_k) {
+      const size_t p = (size_t)t * top_k + lane;
+      __hip_atomic_store(topk_ids + p, r.id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      topk_weights[p] = r.w;
+      ids_lds[p] = r.id;
+    }
+  }
+  if (gridDim.x > 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = threadIdx.x; i < P; i += kThreads)
+      ids_lds[i] = __hip_atomic_load(topk_ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  align_segment(ids_lds, P, E, B, 1, 0, nullptr, sorted, expert_ids, boff_out, counts_out, smem);
+}
+
 }  // namespace
 
 namespace moe_host {
+
+constexpr size_t route_topk_align_lds(int P, int E) {
+  return sizeof(int) *
+         (size_t)(((align_smem_ints(E) + P + 3) & ~3) + kTopkWaves * topk_wave_floats(E));
+}
+// largest dynamic LDS of the fused launch: one full segment, 512 experts
+constexpr size_t kFusedRouteMaxLds = route_topk_align_lds(kAlignPairsPerSegment, 512);
+static_assert(kFusedRouteMaxLds <= 100 * 1024, "fused top-k + align LDS");
+
+hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32_t* arrivals,
+                                   hipStream_t s) {
+  const size_t lds = route_topk_align_lds(r.M * r.top_k, r.E);
+  static bool attr_set = false;   // idempotent; racing first calls set the same value
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_topk_align_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)kFusedRouteMaxLds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(route_topk_align_kernel, dim3(ceil_div_host(r.M, kTopkWaves)), dim3(kThreads),
+                     lds, s, r.logits, r.M, r.E, r.top_k, r.renormalize, a.block_m, r.topk_ids,
+                     r.topk_weights, a.sorted_token_ids, a.expert_ids, a.expert_block_offsets,
+                     a.expert_counts, arrivals);
+  return hipGetLastError();
+}
 
 int align_segments(int P) {
   const int g = (P + kAlignPairsPerSegment - 1) / kAlignPairsPerSegment;
@@ -229,7 +312,7 @@ hipError_t launch_align(const AlignArgs& a, hipStream_t s) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const size_t lds = sizeof(int) * ((size_t)kWaves * a.E + (a.E + 1) + a.E + kWaves);
+  const size_t lds = sizeof(int) * (size_t)align_smem_ints(a.E);
   hipLaunchKernelGGL(align_scatter_kernel, dim3(G), dim3(kThreads), lds, s, a.topk_ids, a.P,
                      a.E, a.block_m, G, a.scratch, a.sorted_token_ids, a.expert_ids,
                      a.expert_block_offsets, a.expert_counts);

@@ -23,9 +23,11 @@ long long sorted_capacity(long long P, int E, int B) {
 }
 
 // Workspace regions of moe_forward for one (M, E, top_k, H, I, block_m).
-// Only the combine arrival counters need clearing before GEMM 2.
+// Only the arrival counters need clearing: the fused top-k + align counter
+// (arrive) and, for the tiled GEMM 2, the combine counters (cnt) after it.
 struct Layout {
-  size_t ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, partial, cnt, total;
+  size_t arrive, ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, partial, cnt;
+  size_t total;
   size_t zero_words;  // 4-byte words of cnt
 };
 
@@ -39,6 +41,7 @@ Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
     return o;
   };
   const size_t cnt_bytes = (size_t)M * ((H + kCounterCols - 1) / kCounterCols) * 4;
+  L.arrive = take(4);
   L.cnt = take(cnt_bytes);
   L.zero_words = cnt_bytes / 4;
   L.partial = take((size_t)P * H * 4);
@@ -65,6 +68,9 @@ int check_sizes(int M, int E, int top_k, int H, int I) {
 }
 
 bool gemm_block_ok(int B) { return B == 16 || B == 64 || B == 128; }
+
+// Small batches run the top-k and the index lists in one launch.
+bool fused_route(int M, int top_k) { return align_segments(M * top_k) == 1; }
 
 // Kernels queued by one GEMM 2 call: streaming = GEMM 2 + per-token sum;
 // tiled = counter clearing (standalone call only) + GEMM 2 with the fused sum.
@@ -265,8 +271,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
-  fill_info(info, B, H, I,
-            M == 0 ? 0 : 3 + (align_segments(M * top_k) > 1 ? 2 : 1) + gemm2_launches(B, false));
+  const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
+  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + gemm2_launches(B, false));
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
   const Layout L = forward_layout(M, E, top_k, H, I, B);
@@ -280,16 +286,21 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   int32_t* boff = reinterpret_cast<int32_t*>(ws + L.boff);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
 
+  // the router-logits kernel clears the arrival counters
+  const size_t zero_words = B == 16 ? 1 : (L.cnt - L.arrive) / 4 + L.zero_words;
   RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
                reinterpret_cast<float*>(ws + L.logits), ids, wts,
-               B == 16 ? nullptr : reinterpret_cast<float*>(ws + L.cnt),
-               B == 16 ? 0 : L.zero_words};
-  MOE_TRY_HIP(launch_route_logits(ra, s));
-  MOE_TRY_HIP(launch_route_topk(ra, s));
+               reinterpret_cast<float*>(ws + L.arrive), zero_words};
   AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
                reinterpret_cast<int32_t*>(ws + L.counts),
                reinterpret_cast<int32_t*>(ws + L.align_scratch)};
-  MOE_TRY_HIP(launch_align(aa, s));
+  MOE_TRY_HIP(launch_route_logits(ra, s));
+  if (fused_route(M, top_k)) {
+    MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive), s));
+  } else {
+    MOE_TRY_HIP(launch_route_topk(ra, s));
+    MOE_TRY_HIP(launch_align(aa, s));
+  }
   GemmArgs g = gemm_args(M, top_k, E, H, I, B);
   g.sorted_token_ids = sorted;
   g.expert_ids = eids;

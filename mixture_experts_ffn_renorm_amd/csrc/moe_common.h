@@ -126,6 +126,161 @@ __device__ __forceinline__ float sum_partials(const float* src, int stride, int 
   return sum;
 }
 
+// LDS ints used by the index-list build of one segment (1024 threads).
+__host__ __device__ constexpr int align_smem_ints(int E) { return 16 * E + (E + 1) + E + 16; }
+
+// Per-wave LDS floats of topk_token: all logits padded to a multiple of 64
+// (only for the many-ties path), 64 lane maxima, 64 candidate logits, 64
+// candidate ids, 32 slot ids, 32 slot logits.
+__host__ __device__ constexpr int topk_wave_floats(int E) { return ((E + 63) & ~63) + 256; }
+
+struct TopkSlot {
+  int id;     // expert of slot lane (lane < top_k)
+  float w;    // its routing weight
+};
+
+namespace topk_detail {
+// Adds to r the count of the 16 values at o that beat v: kMode 0 counts
+// o >= v (all of them precede v's own position), 1 counts o > v (all follow
+// it), 2 counts o > v plus equal values at lower positions (jbase + u < own).
+template <int kMode>
+__device__ __forceinline__ int count16(const float* o, float v, int jbase, int own, int r) {
+  const f32x4* q = reinterpret_cast<const f32x4*>(o);
+  f32x4 c[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) c[u] = q[u];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      const float x = c[u][z];
+      if (kMode == 0) r += x >= v;
+      if (kMode == 1) r += x > v;
+      if (kMode == 2) r += (x > v) | ((x == v) & (jbase + 4 * u + z < own));
+    }
+  return r;
+}
+
+// Rank of v (at position own) among the n values at o, n a multiple of 64
+// padded with -inf: larger values plus equal values at lower positions.
+__device__ __forceinline__ int rank_in(const float* o, int n, float v, int own) {
+  const int blk = own & ~63;
+  int r = 0;
+  for (int j = 0; j < blk; j += 16) r = count16<0>(o + j, v, j, own, r);
+#pragma unroll
+  for (int j = 0; j < 64; j += 16) r = count16<2>(o + blk + j, v, blk + j, own, r);
+  for (int j = blk + 64; j < n; j += 16) r = count16<1>(o + j, v, j, own, r);
+  return r;
+}
+}  // namespace topk_detail
+
+// Router steps for one token, by one wave (page "Mixture of Experts in vLLM
+// - From First Principles to fused_moe", section "One expert, and one
+// token", sub-section "One token uses only 8 experts"): softmax over all E
+// logits, keep the top_k largest in descending order (exact ties -> lower
+// expert id), rescale the kept probabilities to sum 1 if renormalize.
+//
+// Lane l owns logits l, l + 64, ...  The k-th largest of the 64 lane maxima
+// T is a lower bound of the k-th largest logit (k lanes hold a value >= T),
+// so the kept experts are among the candidates >= T, usually little more
+// than k of them.  Candidates are packed in expert order (one ballot per
+// 64-expert block) and each is ranked against the others with broadcast
+// LDS reads (rank = larger logits + equal logits of lower id); rank j < k
+// is slot j.  More than 64 candidates (many exact ties) ranks every logit
+// the same way.  The max is slot 0.  With renormalize the softmax
+// denominator cancels and only the kept exponentials are summed; without
+// it every lane adds its share and a wave sum follows.  E <= 512,
+// top_k <= 32, finite logits.  Returns slot lane's expert and weight on
+// lanes < top_k.
+__device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int top_k,
+                                      int renormalize, float* scratch) {
+  constexpr int kMaxPerLane = 8;
+  const int lane = threadIdx.x & 63;
+  const int nblk = (E + 63) >> 6;
+  float* lw = scratch;                                       // [64 nblk]
+  float* lm = scratch + 64 * nblk;                           // [64]
+  float* c_v = lm + 64;                                      // [64]
+  int* c_id = reinterpret_cast<int*>(c_v + 64);              // [64]
+  int* s_id = c_id + 64;                                     // [32]
+  float* s_l = reinterpret_cast<float*>(s_id + 32);          // [32]
+  float v[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+  }
+  float lmax = v[0];
+#pragma unroll
+  for (int i = 1; i < kMaxPerLane; ++i) lmax = fmaxf(lmax, v[i]);
+  lm[lane] = lmax;
+  __builtin_amdgcn_wave_barrier();
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 16) gt = topk_detail::count16<1>(lm + j, lmax, j, lane, gt);
+  const float T = -wave_max(gt < top_k ? -lmax : -INFINITY);
+
+  // pack the candidates in expert order
+  int C = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    if (i >= nblk) break;
+    const bool cand = lane + 64 * i < E && v[i] >= T;
+    const unsigned long long m = __ballot(cand);
+    const int pos = C + __popcll(m & below);
+    if (cand && pos < 64) {
+      c_v[pos] = v[i];
+      c_id[pos] = lane + 64 * i;
+    }
+    C += __popcll(m);
+  }
+  if (C <= 64) {
+    if (lane >= C) c_v[lane] = -INFINITY;
+    __builtin_amdgcn_wave_barrier();
+    const float my = c_v[lane];
+    int r = 0;
+    for (int j = 0; j < C; j += 16) r = topk_detail::count16<2>(c_v + j, my, j, lane, r);
+    if (lane < C && r < top_k) {
+      s_id[r] = c_id[lane];
+      s_l[r] = my;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (i < nblk) lw[lane + 64 * i] = v[i];
+    __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < nblk; ++i) {
+      const int e = lane + 64 * i;
+      const float vi = lw[e];
+      const int r = topk_detail::rank_in(lw, 64 * nblk, vi, e);
+      if (e < E && r < top_k) {
+        s_id[r] = e;
+        s_l[r] = vi;
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float m = s_l[0];
+  float denom;
+  if (renormalize) {
+    denom = 0.f;
+    for (int q = 0; q < top_k; ++q) denom += __expf(s_l[q] - m);
+  } else {
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (lane + 64 * i < E) ps += __expf(v[i] - m);
+    denom = wave_sum(ps);
+  }
+  TopkSlot out{0, 0.f};
+  if (lane < top_k) {
+    out.id = s_id[lane];
+    out.w = __expf(s_l[lane] - m) / denom;
+  }
+  __builtin_amdgcn_wave_barrier();   // scratch may be reused by the next token
+  return out;
+}
+
 // Workgroups are handed to the 8 XCDs of the chip round-robin (id % 8).
 // Map a linear workgroup id to a logical tile id so that every XCD works on
 // one contiguous range of logical tiles (tiles that share operands then
@@ -173,6 +328,10 @@ constexpr int kAlignMaxSegments = 64;
 int align_segments(int P);
 size_t align_scratch_bytes(int P, int E);
 hipError_t launch_align(const AlignArgs& a, hipStream_t s);
+// Top-k of all tokens and the index lists in one launch (one align segment);
+// arrivals: one int, zero before the launch.
+hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32_t* arrivals,
+                                   hipStream_t s);
 
 struct GemmArgs {
   const uint16_t* a_src;     // GEMM 1: x [M, H]; GEMM 2: act [P, I]

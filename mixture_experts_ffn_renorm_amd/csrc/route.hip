@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   if (!kSplitK && e0 >= E) {
     // no experts for this wave
   } else {
-    constexpr int U = 8;   // k steps whose loads are in flight together
+    constexpr int U = kSplitK ? 16 : 8;   // k steps whose loads are in flight together
     for (int k0 = kbeg; k0 < kend; k0 += 32 * U) {
       u32x4 av[U], bv[U];
 #pragma unroll
@@ -95,67 +95,17 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 }
 
 // Softmax over all E, ordered top-k, renormalize; one wave per token.
-// The token's logits sit in LDS; each lane ranks its own values against all
-// E (rank = number of larger logits, equal logits ordered by expert id), and
-// a value of rank j < k is slot j.  Slot 0 is the largest; exact ties go to
-// the lower expert id.  The probability of a kept expert is
-// exp(l - max) / sum over all E of exp(l' - max); renormalize divides the
-// kept probabilities by their sum.
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int M, int E, int top_k, int renormalize,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
-  constexpr int kMaxE = 512, kMaxPerLane = kMaxE / 64;
-  __shared__ __attribute__((aligned(16))) float s_log[4][kMaxE];
-  __shared__ float s_p[4][32];
-  __shared__ int s_id[4][32];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) float scratch[4][topk_wave_floats(512)];
+  const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
   if (t >= M) return;   // whole wave; no workgroup barrier below
-  float* lw = s_log[w];
-  const float* row = logits + (size_t)t * E;
-  float v[kMaxPerLane];
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
-    if (e < E) lw[e] = v[i];
-    m = fmaxf(m, v[i]);
-  }
-  m = wave_max(m);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
-    if (lane + 64 * i < E) s += __expf(v[i] - m);
-  s = wave_sum(s);
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + 64 * i;
-    if (e >= E) continue;
-    int rank = 0;
-    const float ve = v[i];
-    int j = 0;
-    for (; j + 4 <= E; j += 4) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(lw + j);
-      rank += (o[0] > ve) || (o[0] == ve && j + 0 < e);
-      rank += (o[1] > ve) || (o[1] == ve && j + 1 < e);
-      rank += (o[2] > ve) || (o[2] == ve && j + 2 < e);
-      rank += (o[3] > ve) || (o[3] == ve && j + 3 < e);
-    }
-    for (; j < E; ++j) rank += (lw[j] > ve) || (lw[j] == ve && j < e);
-    if (rank < top_k) {
-      s_id[w][rank] = e;
-      s_p[w][rank] = __expf(ve - m) / s;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (lane < top_k) {
-    const float p = s_p[w][lane];
-    float tot = 0.f;
-    for (int j = 0; j < top_k; ++j) tot += s_p[w][j];
-    topk_ids[(size_t)t * top_k + lane] = s_id[w][lane];
-    topk_weights[(size_t)t * top_k + lane] = renormalize ? p / tot : p;
+  const TopkSlot r = topk_token(logits + (size_t)t * E, E, top_k, renormalize, scratch[w]);
+  if ((threadIdx.x & 63) < top_k) {
+    topk_ids[(size_t)t * top_k + (threadIdx.x & 63)] = r.id;
+    topk_weights[(size_t)t * top_k + (threadIdx.x & 63)] = r.w;
   }
 }
 

@@ -75,6 +75,35 @@ def test_forward_workloads(name, M):
         assert info["k_tail"] == 1       # I = 1408 is not a multiple of 256
 
 
+@pytest.mark.parametrize("M", [16, 64])
+def test_forward_exact_ties_across_lane_blocks(M):
+    """Ties through the fused top-k + index-list launch (one and several
+    workgroups)."""
+    from tests.test_gpu_route_align import check_tied_order, tie_layer
+    lay = tie_layer(M)
+    _, ids, wts, _ = run_forward(lay)
+    ref = mo.route(lay["x"], lay["w_router"], lay["top_k"], True, None)
+    assert check_tied_order(ids, ref["topk_ids"]) >= 2
+    ok = ref["margin"] > h.MARGIN
+    assert np.array_equal(ids[ok], ref["topk_ids"][ok])
+    assert np.abs(wts[ok] - ref["topk_weights"][ok]).max() <= h.WEIGHT_TOL
+
+
+def test_forward_all_logits_equal():
+    """Zero router: every token keeps experts 0..k-1 with weight 1/k, so the
+    layer equals the mean of those experts' FFNs."""
+    lay = wl.make_layer("qwen3_decode", 16)
+    lay["w_router"][:] = 0
+    _, ids, wts, _ = run_forward(lay)
+    k = lay["top_k"]
+    assert np.array_equal(ids, np.tile(np.arange(k, dtype=np.int32), (16, 1)))
+    assert np.abs(wts - 1.0 / k).max() <= 1e-6
+    out, _, _, _ = run_forward(lay)
+    xw = mo.widen_bf16(lay["x"])
+    ref = sum(mo.expert_ffn(xw, lay["w13"][e], lay["w2"][e]) for e in range(k)) / k
+    h.assert_close_outputs(h.host_bf16_to_f64(out), ref)
+
+
 def test_forward_zipf_prefill_has_empty_experts():
     """The skewed prefill layer routes no pair to some experts and very many
     to a few; the layer output still matches."""

@@ -166,6 +166,57 @@ def test_route_exact_ties_lower_id():
         assert row == order.tolist()
 
 
+def tie_layer(M: int):
+    """wide256 layer whose experts 0, 5, 63, 64, 130, 200, 255 share one
+    router row (4x row 17, exact in bf16): their logits tie exactly, inside
+    one 64-expert block and across blocks, and often fill the top 7."""
+    lay = wl.make_layer("wide256", M, I=8)
+    row = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(lay["w_router"][17]) * 4.0)
+    for e in TIED:
+        lay["w_router"][e] = row
+    return lay
+
+
+TIED = [0, 5, 63, 64, 130, 200, 255]
+
+
+def check_tied_order(ids: np.ndarray, ref_ids: np.ndarray) -> int:
+    """Tied experts appear in ascending id order in every token; tokens whose
+    top 7 are the tied group match the oracle exactly.  Returns how many."""
+    full = 0
+    for t in range(ids.shape[0]):
+        row = ids[t].tolist()
+        tied = [e for e in row if e in TIED]
+        assert tied == sorted(tied)
+        if row[:7] == TIED:
+            full += 1
+            assert ref_ids[t][:7].tolist() == TIED
+    return full
+
+
+def test_route_exact_ties_across_lane_blocks():
+    lay = tie_layer(64)
+    ids, _, logits = run_route(lay)
+    assert len({logits[0, e] for e in TIED}) == 1
+    ref = mo.route(lay["x"], lay["w_router"], lay["top_k"], True, None)
+    assert check_tied_order(ids, ref["topk_ids"]) >= 8
+    ok = ref["margin"] > h.MARGIN
+    assert np.array_equal(ids[ok], ref["topk_ids"][ok])
+
+
+@pytest.mark.parametrize("name,M", [("wide256", 16), ("qwen3_decode", 8), ("toy", 3)])
+def test_route_all_logits_equal(name, M):
+    """A zero router makes every logit 0: the kept experts are 0..k-1 in
+    order, with equal weights (1/k renormalized, 1/E without)."""
+    lay = wl.make_layer(name, M, I=8)
+    lay["w_router"][:] = 0
+    E, k = lay["E"], lay["top_k"]
+    for ren in (True, False):
+        ids, wts, _ = run_route(lay, ren)
+        assert np.array_equal(ids, np.tile(np.arange(k, dtype=np.int32), (M, 1)))
+        assert np.abs(wts - (1.0 / k if ren else 1.0 / E)).max() <= 1e-6
+
+
 def test_route_deterministic():
     lay = wl.make_layer("qwen3_prefill", 4096, I=8)
     a = run_route(lay)
