@@ -21,7 +21,9 @@
  * Conventions for every call below.
  *   - bf16 tensors are passed as raw uint16_t bit patterns.
  *   - Every pointer is a DEVICE pointer unless marked "host".  All tensors
- *     are dense, row-major, and 16-byte aligned.
+ *     are dense, row-major, and 16-byte aligned (the GEMM calls and
+ *     moe_forward return MOE_ERR_INVALID_ARG for a misaligned operand,
+ *     index list, output or workspace).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call is asynchronous on that stream: it never allocates, frees or
  *     synchronizes, and returns as soon as its kernels are queued.
@@ -81,7 +83,8 @@ const char* moe_strerror(int status);
 
 /* The block size (block_m) moe_forward uses for a batch of M tokens: the
  * compiled tile table, keyed on the mean number of pairs per expert
- * (M*top_k/E).  Returns 16 (weight-streaming kernels), 64 or 128 (tiled). */
+ * (M*top_k/E).  Returns 16 (weight-streaming kernels), 64, 128 or 256
+ * (tiled). */
 int moe_pick_block_m(int M, int E, int top_k);
 
 /*
@@ -145,8 +148,8 @@ int moe_align(const int32_t* topk_ids, int M, int top_k, int E, int block_m,
  * by row).  The [M*top_k, 2I] GEMM 1 output never exists in memory.
  *
  *   x      [M, H] bf16;  w13 [E, 2I, H] bf16 (gate rows first)
- *   index lists from moe_align with the same block_m (16, 64 or 128;
- *   16 selects the weight-streaming kernel, 64/128 the tiled kernel)
+ *   index lists from moe_align with the same block_m (16, 64, 128 or 256;
+ *   16 selects the weight-streaming kernel, the others the tiled kernel)
  *   act    out [M*top_k, I] bf16 in pair order (row p = t*top_k + j)
  *   info   host, optional: which kernel ran
  * Accumulation is fp32; act is rounded to bf16 once.
@@ -158,20 +161,22 @@ int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
                              uint16_t* act, moe_dispatch_info* info, void* stream);
 
 /*
- * moe_grouped_gemm_w2_combine -- grouped GEMM 2 with the weighted top-k
- * combine fused.  Page "Mixture of Experts in vLLM ...", sections "Put the
- * results back, and combine them per token" and "The rest of the layer
- * stays in pair order" (GEMM 2 reads row p, multiplies by topk_weights[p];
- * the per-token sum).  The [M*top_k, H] GEMM 2 output never exists.
+ * moe_grouped_gemm_w2_combine -- grouped GEMM 2 and the weighted top-k
+ * combine.  Page "Mixture of Experts in vLLM ...", sections "The rest of the
+ * layer stays in pair order" (GEMM 2 reads act row p in place and writes
+ * row p of the pair-order product, the page's cache3) and "Put the results
+ * back, and combine them per token" (moe_sum with the routed weights).
  *
  *   act          [M*top_k, I] bf16 in pair order
  *   w2           [E, H, I] bf16
  *   topk_weights [M*top_k] fp32
  *   out          out [M, H] bf16 in token order
- *   workspace    scratch for the fp32 per-token sums and arrival counters,
- *                ws_bytes >= moe_workspace_size(M, E, top_k, H, I)
- * Each output row is summed in fp32 (in arrival order, so the last bit of
- * the bf16 result may differ between runs) and rounded to bf16 once.
+ *   workspace    holds the pair-order product [M*top_k, H] (block_m 16:
+ *                fp32, already scaled by topk_weights; 64 and 128: bf16,
+ *                scaled in the sum), ws_bytes >= moe_workspace_size(M, E,
+ *                top_k, H, I)
+ * A second kernel adds each token's top_k rows in slot order in fp32 and
+ * rounds once to bf16, so results are bitwise repeatable.
  */
 int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
                                 const float* topk_weights,

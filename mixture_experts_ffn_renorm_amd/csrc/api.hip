@@ -23,12 +23,12 @@ long long sorted_capacity(long long P, int E, int B) {
 }
 
 // Workspace regions of moe_forward for one (M, E, top_k, H, I, block_m).
-// Only the arrival counters need clearing: the fused top-k + align counter
-// (arrive) and, for the tiled GEMM 2, the combine counters (cnt) after it.
+// Only the arrival counter of the fused top-k + align launch needs clearing
+// (done by the router-logits kernel).  partial holds GEMM 2's pair-order
+// rows: fp32 weighted (streaming) or bf16 (tiled).
 struct Layout {
-  size_t arrive, ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, partial, cnt;
+  size_t arrive, ids, wts, logits, sorted, eids, boff, counts, align_scratch, act, partial;
   size_t total;
-  size_t zero_words;  // 4-byte words of cnt
 };
 
 Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
@@ -40,10 +40,7 @@ Layout forward_layout(int M, int E, int top_k, int H, int I, int B) {
     off = align_up(off + bytes);
     return o;
   };
-  const size_t cnt_bytes = (size_t)M * ((H + kCounterCols - 1) / kCounterCols) * 4;
   L.arrive = take(4);
-  L.cnt = take(cnt_bytes);
-  L.zero_words = cnt_bytes / 4;
   L.partial = take((size_t)P * H * 4);
   L.ids = take((size_t)P * 4);
   L.wts = take((size_t)P * 4);
@@ -67,14 +64,23 @@ int check_sizes(int M, int E, int top_k, int H, int I) {
   return MOE_OK;
 }
 
-bool gemm_block_ok(int B) { return B == 16 || B == 64 || B == 128; }
+// Block sizes the GEMM calls accept (16: weight-streaming kernels; the
+// others: tiled kernels).
+constexpr int kBlockSizes[] = {16, 64, 128, 256};
+bool gemm_block_ok(int B) {
+  for (int b : kBlockSizes)
+    if (B == b) return true;
+  return false;
+}
+
+// The kernels copy 16-byte pieces of every tensor.
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Small batches run the top-k and the index lists in one launch.
 bool fused_route(int M, int top_k) { return align_segments(M * top_k) == 1; }
 
-// Kernels queued by one GEMM 2 call: streaming = GEMM 2 + per-token sum;
-// tiled = counter clearing (standalone call only) + GEMM 2 with the fused sum.
-int gemm2_launches(int B, bool standalone) { return B == 16 ? 2 : (standalone ? 2 : 1); }
+// Kernels queued by one GEMM 2 call: the GEMM and the per-token weighted sum.
+constexpr int kGemm2Launches = 2;
 
 void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches) {
   if (info == nullptr) return;
@@ -139,8 +145,7 @@ extern "C" {
 size_t moe_workspace_size(int M_max, int E, int top_k, int H, int I) {
   if (check_sizes(M_max, E, top_k, H, I) != MOE_OK) return 0;
   size_t best = 0;
-  for (int B : {16, 64, 128})
-    best = std::max(best, forward_layout(M_max, E, top_k, H, I, B).total);
+  for (int B : kBlockSizes) best = std::max(best, forward_layout(M_max, E, top_k, H, I, B).total);
   return std::max<size_t>(best, kAlign);
 }
 
@@ -160,7 +165,8 @@ int moe_pick_block_m(int M, int E, int top_k) {
   const double per_expert = (double)M * top_k / E;
   if (per_expert <= 8.0) return 16;
   if (per_expert <= 48.0) return 64;
-  return 128;
+  if (per_expert < 128.0) return 128;
+  return 256;
 }
 
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bias, int M,
@@ -219,6 +225,7 @@ int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
   if (M == 0) return MOE_OK;
   if (!x || !w13 || !sorted_token_ids || !expert_ids || !expert_block_offsets || !act)
     return MOE_ERR_INVALID_ARG;
+  if (!a16(x) || !a16(w13) || !a16(sorted_token_ids) || !a16(act)) return MOE_ERR_INVALID_ARG;
   GemmArgs g = gemm_args(M, top_k, E, H, I, block_m);
   g.a_src = x;
   g.w = w13;
@@ -238,18 +245,18 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
   int st = check_sizes(M, E, top_k, H, I);
   if (st != MOE_OK) return st;
   if (!gemm_block_ok(block_m)) return MOE_ERR_UNSUPPORTED;
-  fill_info(info, block_m, H, I, M == 0 ? 0 : gemm2_launches(block_m, true));
+  fill_info(info, block_m, H, I, M == 0 ? 0 : kGemm2Launches);
   if (M == 0) return MOE_OK;
   if (!act || !w2 || !topk_weights || !sorted_token_ids || !expert_ids ||
       !expert_block_offsets || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!a16(act) || !a16(w2) || !a16(sorted_token_ids) || !a16(out) || !a16(workspace))
     return MOE_ERR_INVALID_ARG;
   const Layout L = forward_layout(M, E, top_k, H, I, block_m);
   const size_t need = L.partial + (size_t)M * top_k * H * 4;
   if (workspace == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if (block_m != 16)   // the tiled kernel's fused sum counts arrivals
-    MOE_TRY_HIP(launch_fill_zero(reinterpret_cast<float*>(ws + L.cnt), L.zero_words, s));
   GemmArgs g = gemm_args(M, top_k, E, H, I, block_m);
   g.a_src = act;
   g.w = w2;
@@ -259,7 +266,6 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
   g.expert_block_offsets = expert_block_offsets;
   g.out = out;
   g.partial = reinterpret_cast<float*>(ws + L.partial);
-  g.counters = reinterpret_cast<int32_t*>(ws + L.cnt);
   return run_gemm2(g, s);
 }
 
@@ -272,9 +278,11 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
-  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + gemm2_launches(B, false));
+  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches);
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+  if (!a16(x) || !a16(w_router) || !a16(w13) || !a16(w2) || !a16(out) || !a16(workspace))
+    return MOE_ERR_INVALID_ARG;
   const Layout L = forward_layout(M, E, top_k, H, I, B);
   if (workspace == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -286,11 +294,10 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   int32_t* boff = reinterpret_cast<int32_t*>(ws + L.boff);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
 
-  // the router-logits kernel clears the arrival counters
-  const size_t zero_words = B == 16 ? 1 : (L.cnt - L.arrive) / 4 + L.zero_words;
+  // the router-logits kernel clears the arrival counter
   RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
                reinterpret_cast<float*>(ws + L.logits), ids, wts,
-               reinterpret_cast<float*>(ws + L.arrive), zero_words};
+               reinterpret_cast<float*>(ws + L.arrive), 1};
   AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
                reinterpret_cast<int32_t*>(ws + L.counts),
                reinterpret_cast<int32_t*>(ws + L.align_scratch)};
@@ -315,7 +322,6 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   g.topk_weights = wts;
   g.out = out;
   g.partial = reinterpret_cast<float*>(ws + L.partial);
-  g.counters = reinterpret_cast<int32_t*>(ws + L.cnt);
   return run_gemm2(g, s);
 }
 

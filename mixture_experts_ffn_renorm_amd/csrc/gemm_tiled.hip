@@ -1,35 +1,51 @@
 // LDS-tiled MFMA grouped GEMMs for batches with many pairs per expert.
 //
 // GEMM 1 (page "Mixture of Experts in vLLM - From First Principles to
-// fused_moe", sub-section "One GEMM 1 program, step by step"): a workgroup
-// owns one block of BM pairs (one expert, from the index lists) and 128
-// columns of the activation.  It reads expert_ids[b], skips pad entries
+// fused_moe", sub-section "One GEMM 1 program, step by step"): a tile is one
+// block of BM pairs (one expert, from the index lists) and 128 columns of
+// the activation.  It reads expert_ids[b], skips pad entries
 // (id >= M*top_k), reads input row p // top_k of x in place, multiplies by
 // the matching 128 gate rows and 128 up rows of W13[e], and writes
 // SiLU(gate) * up to row p of act (sub-section "The rest of the layer stays
 // in pair order"), so the [M*top_k, 2I] product never reaches memory.
 //
-// GEMM 2 (same page, "The rest of the layer stays in pair order" and "Put
-// the results back, and combine them per token"): the same tiling over
-// act (row p read directly) and 256 rows of W2[e]; the epilogue scales row p
-// by topk_weights[p] and stores it as an fp32 partial row p; the last of the
-// top_k workgroups that produce a (token, 64-column group) adds that
-// token's top_k partial rows in slot order and writes the bf16 output row
-// piece in token order (no separate sum kernel, no atomic adds on data).
+// GEMM 2 (same page, "The rest of the layer stays in pair order"): the same
+// tiling over act (row p read directly) and 256 rows of W2[e]; row p of the
+// bf16 pair-order product [M*top_k, H] is written in place (the page's
+// cache3).  A second small kernel reads, per token, its top_k rows and adds
+// them weighted by topk_weights in slot order (section "Put the results
+// back, and combine them per token": moe_sum with the routed weights).
 //
-// Tile: 256 weight rows x BM pairs x 64 k per stage, 8 waves in a 4 x 2
-// layout, each wave 64 weight rows x BM/2 pairs of 16x16x32 bf16 MFMAs.
-// Weights are the MFMA A operand and pairs the B operand, so each lane ends
-// with 4 consecutive features of one pair.
+// Tile: 256 weight rows x BM pairs (BM = 64, 128 or 256) x 64 k per stage,
+// 8 waves in a 4 x 2 layout, each wave 64 weight rows x BM/2 pairs of
+// 16x16x32 bf16 MFMAs.  Weights are the MFMA A operand and pairs the B
+// operand, so each lane ends with 4 consecutive features of one pair.  With
+// BM = 256 an expert of up to 256 pairs reads each weight tile once, and
+// each k step of LDS operands feeds twice the MFMAs of BM = 128 (measured:
+// about 1.3x the rate).  A wave group whose half of the block holds only
+// pads (the tail of an expert's last block) skips its MFMAs.
 //
-// Memory pipeline: operands go from global memory straight into LDS with
-// global_load_lds_dwordx4 (no register staging), three stages deep.  One
-// load instruction of a wave fills 1 KB of LDS = 8 rows of 64 k values; a
-// row's eight 16-byte chunks are stored XOR-swizzled (chunk c of row R at
-// slot c ^ ((R >> 1) & 7)), so the 16 rows that one MFMA operand read
-// touches fall on distinct banks, while each global access still reads
-// whole 128-byte row pieces.  Rows or k ranges outside the operands (pads,
-// features past the end, the K tail) load from a zeroed 16-byte page.
+// Persistent workgroups, one per CU.  Each XCD owns a contiguous range of
+// tiles (block-major, all column tiles of a block side by side) and its
+// workgroups take them round robin, so the column tiles of one block (same
+// gathered rows) and the same column tile of an expert's adjacent blocks
+// (same weights) run together under one L2.  A workgroup streams its whole
+// sequence of (tile, k-step) stages through one LDS ring (3 stages; 2 of
+// 64 KB for BM = 256): the loads of the next tile start while the current
+// one finishes and runs its epilogue.  A tile's pair ids and expert id are
+// copied into LDS by the same asynchronous copies two tiles ahead.
+//
+// Copies go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register staging).  One copy instruction of a
+// wave fills 1 KB of LDS = 8 rows of 64 k values; a row's eight 16-byte
+// chunks are stored XOR-swizzled (chunk c of row R at slot c ^ ((R >> 1) &
+// 7)), so the 16 rows that one MFMA operand read touches fall on distinct
+// banks, while each global access still reads whole 128-byte row pieces.
+// Rows or k ranges outside the operands (pads, features past the end, the K
+// tail) copy a zeroed 16-byte page.
+#include <algorithm>
+#include <type_traits>
+
 #include "moe_common.h"
 
 using namespace moe;
@@ -37,20 +53,25 @@ using namespace moe;
 namespace {
 
 constexpr int kBK = 64;          // k elements per stage = 128 bytes per row
-constexpr int kBN = 256;         // weight rows per tile
-constexpr int kStages = 3;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowBytes = kBK * 2;
+constexpr int kMeta = 5;         // tile metadata buffers (pair ids, expert)
 
+// Tile shape per block size BM: 256 weight rows x BM pairs, waves in a
+// 4 (features, 64 rows each) x 2 (pair halves) layout.
 template <int BM>
 struct TileCfg {
-  static constexpr int kWGroups = kBN / 8 / kWaves;   // 8-row W groups per wave (4)
-  static constexpr int kXGroups = BM / 8 / kWaves;    // 8-row X groups per wave (2 or 1)
-  static constexpr int kLoads = kWGroups + kXGroups;  // load instructions per stage
-  static constexpr int kStageBytes = (kBN + BM) * kRowBytes;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kNT = BM / 32;                 // 16-pair MFMA tiles per wave
+  static constexpr int kBN = 256;                      // weight rows per tile
+  static constexpr int kWF = kBN / 64;
+  static constexpr int kWP = kWaves / kWF;
+  static constexpr int kWGroups = kBN / 8 / kWaves;   // 8-row W groups per wave (2 or 4)
+  static constexpr int kXGroups = BM / 8 / kWaves;    // 8-row X groups per wave (1, 2 or 4)
+  static constexpr int kLoads = kWGroups + kXGroups;  // copy instructions per stage
+  static constexpr int kStageBytes = (kBN + BM) * kRowBytes;   // 40, 48 or 64 KB
+  static constexpr int kStages = BM == 256 ? 2 : 3;    // ring within 160 KB of LDS
+  static constexpr int kRingBytes = kStages * kStageBytes;
+  static constexpr int kNT = BM / kWP / 16;           // 16-pair MFMA tiles per wave
 };
 
 // Slot of a row's 16-byte chunk: chunk c of row R sits at c ^ swz(R).  With
@@ -60,124 +81,148 @@ struct TileCfg {
 // stride, or the XOR with (R ^ (R >> 3)) & 7, both run at about half).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// Each active lane copies 4 bytes from src to LDS at lds_dst + 4 * lane.
+__device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 4, 0, 0);
+}
+
 struct TileParams {
-  const uint16_t* a_src;
-  const uint16_t* w;
+  const uint16_t* a_src;   // GEMM 1: x [M, H]; GEMM 2: act [P, I]
+  const uint16_t* w;       // GEMM 1: w13 [E, 2I, H]; GEMM 2: w2 [E, H, I]
   const int32_t* sorted;
   const int32_t* expert_ids;
   const int32_t* boff;
-  const float* topk_weights;
   int M, top_k, E, H, I;
-  int ntiles_n;        // feature tiles per block
-  uint16_t* out;
-  float* partial;      // GEMM 2: [M*top_k, H] fp32 weighted partial rows
-  int32_t* counters;
+  int ntn;                 // column tiles per block
+  uint16_t* out;           // GEMM 1: act [P, I]; GEMM 2: pair-order product [P, H]
 };
 
 template <int BM, bool kGemm1>
-__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(TileParams prm) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParams prm) {
   using C = TileCfg<BM>;
   constexpr int NT = C::kNT;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int s_pair[BM];
-  __shared__ float s_wt[BM];
-  __shared__ int s_last[4 * BM];
+  constexpr int kStages = C::kStages;
+  constexpr int kBN = C::kBN;
+  constexpr int kHalf = kBN / 2;   // GEMM 1: gate rows, then as many up rows
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  __shared__ __attribute__((aligned(16))) int s_pair[kMeta][BM];
+  __shared__ int s_exp[kMeta];
 
   const int P = prm.M * prm.top_k;
-  const int nblocks = prm.boff[prm.E];
-  const int tile = xcd_contiguous_tile(blockIdx.x, nblocks * prm.ntiles_n);
-  if (tile < 0) return;
-  const int b = tile / prm.ntiles_n;
-  const int nt = tile - b * prm.ntiles_n;
-  const int e = prm.expert_ids[b];
   const int K = kGemm1 ? prm.H : prm.I;
+  const int ntn = prm.ntn;
+  const int njobs = prm.boff[prm.E] * ntn;
+  // tiles of this workgroup: j0, j0 + nslots, ... inside its XCD's range
+  const int xcd = blockIdx.x & 7, nslots = gridDim.x >> 3, myslot = blockIdx.x >> 3;
+  const int chunk = ceil_div(njobs, 8);
+  const int j0 = xcd * chunk + myslot;
+  const int jend = min(njobs, (xcd + 1) * chunk);
+  if (j0 >= jend) return;   // whole workgroup
+  const int nmine = ceil_div(jend - j0, nslots);
+  const int nk = ceil_div(K, kBK);
+  const int G = nmine * nk;  // stages of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-
-  if (tid < BM) {
-    const int p = prm.sorted[b * BM + tid];
-    s_pair[tid] = p;
-    s_wt[tid] = (!kGemm1 && p < P) ? prm.topk_weights[p] : 0.f;
-  }
-
-  // ---- per-lane source row of each load slot (row R of the LDS tile) ----
   const int lrow = lane >> 3, lpos = lane & 7;
-  const uint16_t* wsrc[C::kWGroups];
-  int wchunk[C::kWGroups];
-#pragma unroll
-  for (int i = 0; i < C::kWGroups; ++i) {
-    const int R = (wv + kWaves * i) * 8 + lrow;
-    wchunk[i] = lpos ^ swz(R);
-    const uint16_t* row = nullptr;
-    if (kGemm1) {
-      const int f = nt * 128 + (R & 127);
-      if (f < prm.I)
-        row = prm.w + ((size_t)e * 2 * prm.I + (R < 128 ? f : prm.I + f)) * K;
-    } else {
-      const int h = nt * kBN + R;
-      if (h < prm.H) row = prm.w + ((size_t)e * prm.H + h) * K;
-    }
-    wsrc[i] = row;
-  }
-  const uint16_t* xsrc[C::kXGroups];
-  int xchunk[C::kXGroups];
-#pragma unroll
-  for (int i = 0; i < C::kXGroups; ++i) {
-    const int R = (wv + kWaves * i) * 8 + lrow;
-    xchunk[i] = lpos ^ swz(R);
-    const int p = prm.sorted[b * BM + R];
-    const uint16_t* row = nullptr;
-    if (p < P)
-      row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * prm.H
-                   : prm.a_src + (size_t)p * prm.I;
-    xsrc[i] = row;
-  }
 
-  auto issue_stage = [&](int kt, int buf) {
-    uint8_t* sb = lds + buf * C::kStageBytes;
+  // ---- metadata copies of tile i into buffer i % kMeta ----
+  auto issue_meta = [&](int i) {
+    if (i >= nmine) return;
+    const int b = (j0 + i * nslots) / ntn;
+    if (wv == 0 && lane < BM / 4)
+      load_lds16(prm.sorted + (size_t)b * BM + 4 * lane, reinterpret_cast<uint8_t*>(s_pair[i % kMeta]));
+    if (wv == 1 && lane == 0) load_lds4(prm.expert_ids + b, &s_exp[i % kMeta]);
+  };
+
+  // ---- per-lane copy sources of the tile being issued ----
+  int wchunk[C::kWGroups], xchunk[C::kXGroups];
 #pragma unroll
-    for (int i = 0; i < C::kWGroups; ++i) {
-      const int k = kt * kBK + wchunk[i] * 8;
-      const void* src = (wsrc[i] != nullptr && k < K) ? (const void*)(wsrc[i] + k)
-                                                      : (const void*)kZeroPage;
-      load_lds16(src, sb + (wv + kWaves * i) * 8 * kRowBytes);
+  for (int i = 0; i < C::kWGroups; ++i) wchunk[i] = lpos ^ swz((wv + kWaves * i) * 8 + lrow);
+#pragma unroll
+  for (int i = 0; i < C::kXGroups; ++i) xchunk[i] = lpos ^ swz((wv + kWaves * i) * 8 + lrow);
+  const uint16_t* wsrc[C::kWGroups];
+  const uint16_t* xsrc[C::kXGroups];
+
+  // Point the copy sources at tile i (its metadata is in LDS), and start the
+  // metadata copies of tile i + 2.
+  auto setup = [&](int i) {
+    const int buf = i % kMeta;
+    const int j = j0 + i * nslots;
+    const int nt = j - (j / ntn) * ntn;
+    const int e = s_exp[buf];
+#pragma unroll
+    for (int gi = 0; gi < C::kWGroups; ++gi) {
+      const int R = (wv + kWaves * gi) * 8 + lrow;
+      const uint16_t* row = nullptr;
+      if (kGemm1) {
+        const int f = nt * kHalf + (R % kHalf);
+        if (f < prm.I)
+          row = prm.w + ((size_t)e * 2 * prm.I + (R < kHalf ? f : prm.I + f)) * K;
+      } else {
+        const int h = nt * kBN + R;
+        if (h < prm.H) row = prm.w + ((size_t)e * prm.H + h) * K;
+      }
+      wsrc[gi] = row;
     }
 #pragma unroll
-    for (int i = 0; i < C::kXGroups; ++i) {
-      const int k = kt * kBK + xchunk[i] * 8;
-      const void* src = (xsrc[i] != nullptr && k < K) ? (const void*)(xsrc[i] + k)
-                                                      : (const void*)kZeroPage;
-      load_lds16(src, sb + (kBN + (wv + kWaves * i) * 8) * kRowBytes);
+    for (int gi = 0; gi < C::kXGroups; ++gi) {
+      const int R = (wv + kWaves * gi) * 8 + lrow;
+      const int p = s_pair[buf][R];
+      const uint16_t* row = nullptr;
+      if (p < P)
+        row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * prm.H
+                     : prm.a_src + (size_t)p * prm.I;
+      xsrc[gi] = row;
+    }
+    issue_meta(i + 2);
+  };
+
+  int is_i = 0, is_kt = 0, is_slot = 0;
+  auto issue_stage = [&](int g) {
+    const int i = is_i, kt = is_kt;
+    if (kt == 0) setup(i);
+    uint8_t* sb = ring + is_slot * C::kStageBytes;
+    is_slot = is_slot == kStages - 1 ? 0 : is_slot + 1;
+    if (++is_kt == nk) { is_kt = 0; ++is_i; }
+#pragma unroll
+    for (int gi = 0; gi < C::kWGroups; ++gi) {
+      const int k = kt * kBK + wchunk[gi] * 8;
+      const void* src = (wsrc[gi] != nullptr && k < K) ? (const void*)(wsrc[gi] + k)
+                                                        : (const void*)kZeroPage;
+      load_lds16(src, sb + (wv + kWaves * gi) * 8 * kRowBytes);
+    }
+#pragma unroll
+    for (int gi = 0; gi < C::kXGroups; ++gi) {
+      const int k = kt * kBK + xchunk[gi] * 8;
+      const void* src = (xsrc[gi] != nullptr && k < K) ? (const void*)(xsrc[gi] + k)
+                                                        : (const void*)kZeroPage;
+      load_lds16(src, sb + (kBN + (wv + kWaves * gi) * 8) * kRowBytes);
     }
   };
 
   // ---- this wave's MFMA tiles ----
-  const int wf = wv & 3, wp = wv >> 2;
-  int arow[4];
-  if (kGemm1) {
-    arow[0] = wf * 32;        arow[1] = wf * 32 + 16;         // gate rows
-    arow[2] = 128 + wf * 32;  arow[3] = 128 + wf * 32 + 16;   // matching up rows
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = wf * 64 + 16 * i;
-  }
-  const int brow0 = wp * (BM / 2);
+  // A tiles (weight rows): GEMM 1 gate rows wf*32 + {0, 16} and the matching
+  // up rows kHalf + wf*32 + {0, 16}; GEMM 2 rows wf*64 + {0, 16, 32, 48}.
+  // B tiles (pairs): rows wp * BM/2 + 16 j, j < NT: the wave group wp owns
+  // one half of the block, and skips its MFMAs when that half holds only
+  // pads (the tail of an expert's last block); the two waves that share a
+  // SIMD own different halves, so a half-empty block takes about half the
+  // time.  Every tile starts at a multiple of 16 rows, so a lane's swizzle
+  // depends only on r16 and each tile's offset is a constant added to one
+  // base per operand and k half.
+  const int wf = wv % C::kWF, wp = wv / C::kWF;
   const int r16 = lane & 15, kg = lane >> 4;
-  // byte offsets inside a stage of this lane's operand reads, per k half s
-  int aoff[2][4], boffs[2][NT];
+  auto brow = [&](int j) { return wp * (BM / 2) + 16 * j; };   // first pair of B tile j
+  const int arow0 = kGemm1 ? wf * 32 : wf * 64;
+  int abase[2], bbase[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int c = s * 4 + kg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int R = arow[i] + r16;
-      aoff[s][i] = R * kRowBytes + ((c ^ swz(R)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int R = brow0 + 16 * j + r16;
-      boffs[s][j] = (kBN + R) * kRowBytes + ((c ^ swz(R)) << 4);
-    }
+    const int slot = ((s * 4 + kg) ^ swz(r16)) << 4;
+    abase[s] = (arow0 + r16) * kRowBytes + slot;
+    bbase[s] = (kBN + wp * (BM / 2) + r16) * kRowBytes + slot;
   }
+  auto aconst = [](int i) {
+    return (kGemm1 ? (i >> 1) * kHalf + (i & 1) * 16 : 16 * i) * kRowBytes;
+  };
 
   f32x4 acc[4][NT];
 #pragma unroll
@@ -185,133 +230,146 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(TileParams prm)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = ceil_div(K, kBK);
-  issue_stage(0, 0);
-  if (nk > 1) issue_stage(1, 1);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the next stage's loads are pending
-    if (kt + 1 < nk) wait_vmem<C::kLoads>(); else wait_vmem<0>();
-    // Every wave's part of stage kt is in LDS, and stage kt-1 is consumed.
-    barrier_nofence();
-    if (kt + 2 < nk) issue_stage(kt + 2, (kt + 2) % kStages);
-    const uint8_t* sb = lds + (kt % kStages) * C::kStageBytes;
+  // ---- prologue: metadata of tiles 0 and 1, then the first kStages-1 stages ----
+  issue_meta(0);
+  issue_meta(1);
+  wait_vmem<0>();
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < kStages - 1; ++g)
+    if (g < G) issue_stage(g);
+
+  bool active = true;   // this wave's half of the block holds a pair
+  // One stage of MFMAs over the first NA B tiles, fully unrolled.
+  auto compute = [&](auto na, const uint8_t* sb) {
+    constexpr int NA = decltype(na)::value;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4 af[4], bfr[NT];
+      u32x4 af[4], bfr[NA > 0 ? NA : 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + aoff[s][i]);
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + aconst(i));
 #pragma unroll
-      for (int j = 0; j < NT; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(sb + boffs[s][j]);
+      for (int j = 0; j < NA; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] + j * 16 * kRowBytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < NA; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
     }
-  }
+  };
+  int c_i = 0, c_kt = 0, c_buf = 0, c_slot = 0;
+  for (int g = 0; g < G; ++g) {
+    // stage g has landed once at most the later stages' copies are pending
+    if (kStages == 3 && g + 1 < G) wait_vmem<C::kLoads>(); else wait_vmem<0>();
+    // Every wave's part of stage g is in LDS, and stage g-1 is consumed.
+    barrier_nofence();
+    if (g + kStages - 1 < G) issue_stage(g + kStages - 1);
+    const int i_tile = c_i, kt = c_kt;
+    const int buf = c_buf;
+    if (kt == 0) {
+      bool any = false;
+#pragma unroll
+      for (int r = lane; r < BM / 2; r += 64) any |= s_pair[buf][wp * (BM / 2) + r] < P;
+      active = __ballot(any) != 0ull;
+    }
+    const uint8_t* sb = ring + c_slot * C::kStageBytes;
+    if (active) compute(std::integral_constant<int, NT>{}, sb);
+    c_slot = c_slot == kStages - 1 ? 0 : c_slot + 1;
+    if (++c_kt == nk) { c_kt = 0; ++c_i; c_buf = c_buf == kMeta - 1 ? 0 : c_buf + 1; }
+    if (kt != nk - 1) continue;
 
-  // ---- epilogues: lane holds features 4*kg + q of each A tile, pair r16 of each B tile ----
-  if (kGemm1) {
-    const int I = prm.I;
+    // ---- tile epilogue: lane holds features 4*kg + q of each A tile, pair r16 of each B tile ----
+    const int jt = j0 + i_tile * nslots;
+    const int nt = jt - (jt / ntn) * ntn;
+    if (!active) continue;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int p = s_pair[brow0 + 16 * j + r16];
-      if (p >= P) continue;
+      const int p = s_pair[buf][brow(j) + r16];
+      if (p < P) {
+        if (kGemm1) {
+          const int I = prm.I;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int n = nt * 128 + wf * 32 + 16 * i + 4 * kg;
-        if (n >= I) continue;
-        const f32x4 gt = acc[i][j], up = acc[i + 2][j];
-        u32x2 v;
-        v[0] = pack_bf16x2(silu_mul(gt[0], up[0]), silu_mul(gt[1], up[1]));
-        v[1] = pack_bf16x2(silu_mul(gt[2], up[2]), silu_mul(gt[3], up[3]));
-        *reinterpret_cast<u32x2*>(prm.out + (size_t)p * I + n) = v;
+          for (int i = 0; i < 2; ++i) {
+            const int n = nt * kHalf + wf * 32 + 16 * i + 4 * kg;
+            if (n >= I) continue;
+            const f32x4 gt = acc[i][j], up = acc[i + 2][j];
+            u32x2 v;
+            v[0] = pack_bf16x2(silu_mul(gt[0], up[0]), silu_mul(gt[1], up[1]));
+            v[1] = pack_bf16x2(silu_mul(gt[2], up[2]), silu_mul(gt[3], up[3]));
+            *reinterpret_cast<u32x2*>(prm.out + (size_t)p * I + n) = v;
+          }
+        } else {
+          const int H = prm.H;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = nt * kBN + wf * 64 + 16 * i + 4 * kg;
+            if (h >= H) continue;
+            u32x2 v;
+            v[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            v[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            *reinterpret_cast<u32x2*>(prm.out + (size_t)p * H + h) = v;
+          }
+        }
       }
-    }
-    return;
-  }
-
-  // GEMM 2: the wave's 64 x BM/2 tile goes through LDS so that each store
-  // instruction writes 64 consecutive columns of one partial row.  Row p of
-  // the fp32 partials holds topk_weights[p] * (W2[e] act[p]); the stores are
-  // agent-coherent, so other workgroups' coherent loads see them once they
-  // have completed.
-  const int H = prm.H;
-  constexpr int kCt = 65;                           // row stride in floats
-  __syncthreads();                                  // all waves done reading the stages
-  float* ct = reinterpret_cast<float*>(lds) + wv * (BM / 2) * kCt;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ct[(16 * j + r16) * kCt + 16 * i + 4 * kg + q] = acc[i][j][q];
-  __builtin_amdgcn_wave_barrier();
-  const int h = nt * kBN + wf * 64 + lane;
-  if (h < H) {
-    for (int pr = 0; pr < BM / 2; ++pr) {
-      const int p = s_pair[brow0 + pr];
-      if (p >= P) continue;
-      __hip_atomic_store(prm.partial + (size_t)p * H + h, s_wt[brow0 + pr] * ct[pr * kCt + lane],
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < 4; ++i) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  }
-
-  // The last arrival per (token, 64-column group) sums the token's top_k
-  // partial rows in slot order and writes the bf16 result.  Every wave first
-  // waits until its own stores have completed; the workgroup then counts
-  // its arrivals (4 column groups per tile).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const int ncg = ceil_div(H, 64);
-  for (int it = tid; it < 4 * BM; it += kThreads) {
-    const int r = it % BM, cgl = it / BM;
-    const int cg = nt * 4 + cgl;
-    const int p = s_pair[r];
-    int last = -1;
-    if (p < P && cg < ncg) {
-      const int t = p / prm.top_k;
-      const int old = atomicAdd(prm.counters + (size_t)t * ncg + cg, 1);
-      if (old == prm.top_k - 1) last = t;
-    }
-    s_last[it] = last;
-  }
-  __syncthreads();
-  for (int it = wv; it < 4 * BM; it += kWaves) {
-    const int t = s_last[it];
-    if (t < 0) continue;
-    const int col = (nt * 4 + it / BM) * 64 + lane;
-    if (col < H)
-      prm.out[(size_t)t * H + col] =
-          (uint16_t)f32_to_bf16(sum_partials(prm.partial + (size_t)t * prm.top_k * H + col, H,
-                                             prm.top_k));
   }
 }
 
-// the GEMM 2 epilogue reuses the stage LDS for 8 waves x (BM/2) x 65 floats
-static_assert(TileCfg<64>::kLdsBytes >= kWaves * 32 * 65 * 4, "epilogue LDS");
-static_assert(TileCfg<128>::kLdsBytes >= kWaves * 64 * 65 * 4, "epilogue LDS");
+// out[t, h] = bf16(sum over slots j of topk_weights[t, j] * rows[t*top_k + j, h]),
+// j ascending, fp32 sum.  Page "Mixture of Experts in vLLM ...", section
+// "Put the results back, and combine them per token".  Thread: 8
+// consecutive columns of one token (H % 8 == 0).
+__global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __restrict__ rows,
+                                                           const float* __restrict__ topk_weights,
+                                                           int M, int top_k, int H,
+                                                           uint16_t* __restrict__ out) {
+  const int h8 = H / 8;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)M * h8) return;
+  const int t = (int)(i / h8), h = (int)(i - (long long)t * h8) * 8;
+  const uint16_t* src = rows + (size_t)t * top_k * H + h;
+  float sum[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) sum[q] = 0.f;
+  for (int j = 0; j < top_k; ++j) {
+    const float w = topk_weights[(size_t)t * top_k + j];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)j * H);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sum[2 * q] += w * __uint_as_float(v[q] << 16);
+      sum[2 * q + 1] += w * __uint_as_float(v[q] & 0xffff0000u);
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(sum[2 * q], sum[2 * q + 1]);
+  *reinterpret_cast<u32x4*>(out + (size_t)t * H + h) = o;
+}
 
 template <int BM, bool kGemm1>
-hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s) {
+hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* out) {
+  constexpr int kBN = TileCfg<BM>::kBN;
   TileParams prm;
   prm.a_src = a.a_src;
   prm.w = a.w;
   prm.sorted = a.sorted_token_ids;
   prm.expert_ids = a.expert_ids;
   prm.boff = a.expert_block_offsets;
-  prm.topk_weights = a.topk_weights;
   prm.M = a.M;
   prm.top_k = a.top_k;
   prm.E = a.E;
   prm.H = a.H;
   prm.I = a.I;
-  prm.ntiles_n = kGemm1 ? moe_host::ceil_div_host(a.I, 128) : moe_host::ceil_div_host(a.H, kBN);
-  prm.out = a.out;
-  prm.partial = a.partial;
-  prm.counters = a.counters;
-  const long long tiles = (long long)a.max_blocks * prm.ntiles_n;
-  const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-  const size_t lds = TileCfg<BM>::kLdsBytes;
+  prm.ntn = kGemm1 ? moe_host::ceil_div_host(a.I, kBN / 2) : moe_host::ceil_div_host(a.H, kBN);
+  prm.out = out;
+  // persistent grid: one workgroup per CU, never more than the tiles, a multiple of 8
+  const long long tiles = (long long)a.max_blocks * prm.ntn;
+  long long grid = std::min<long long>(tiles, moe_host::device_cu_count());
+  grid = std::max<long long>(8, (grid + 7) / 8 * 8);
+  const size_t lds = TileCfg<BM>::kRingBytes;
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(
@@ -320,7 +378,8 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1>), dim3(grid), dim3(kThreads), lds, s, prm);
+  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1>), dim3((unsigned)grid), dim3(kThreads), lds, s,
+                     prm);
   return hipGetLastError();
 }
 
@@ -329,13 +388,21 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s) {
 namespace moe_host {
 
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s) {
-  if (a.block_m == 128) return launch_tiled<128, true>(a, s);
-  return launch_tiled<64, true>(a, s);
+  if (a.block_m == 256) return launch_tiled<256, true>(a, s, a.out);
+  if (a.block_m == 128) return launch_tiled<128, true>(a, s, a.out);
+  return launch_tiled<64, true>(a, s, a.out);
 }
 
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
-  if (a.block_m == 128) return launch_tiled<128, false>(a, s);
-  return launch_tiled<64, false>(a, s);
+  uint16_t* rows = reinterpret_cast<uint16_t*>(a.partial);
+  hipError_t err = a.block_m == 256   ? launch_tiled<256, false>(a, s, rows)
+                    : a.block_m == 128 ? launch_tiled<128, false>(a, s, rows)
+                                       : launch_tiled<64, false>(a, s, rows);
+  if (err != hipSuccess) return err;
+  const long long n8 = (long long)a.M * (a.H / 8);
+  hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, rows,
+                     a.topk_weights, a.M, a.top_k, a.H, a.out);
+  return hipGetLastError();
 }
 
 }  // namespace moe_host

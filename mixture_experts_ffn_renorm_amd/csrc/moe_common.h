@@ -308,7 +308,7 @@ struct RouteArgs {
   float* logits;        // [M, E] scratch or caller output
   int32_t* topk_ids;    // [M, top_k]
   float* topk_weights;  // [M, top_k]
-  float* zero_ptr;      // optional region to clear (combine arrival counters)
+  float* zero_ptr;      // optional region to clear (arrival counter of the fused top-k + align)
   size_t zero_words;    // number of 4-byte words to clear
 };
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s);
@@ -342,23 +342,21 @@ struct GemmArgs {
   const float* topk_weights; // GEMM 2 only
   int M, top_k, E, H, I, block_m, max_blocks;
   uint16_t* out;             // GEMM 1: act [P, I]; GEMM 2: out [M, H]
-  float* partial;            // GEMM 2: fp32 weighted partial rows [P, H]
-  int32_t* counters;         // GEMM 2: arrival counters [M, ceil(H/64)] (zeroed)
+  float* partial;            // GEMM 2: pair-order rows [P, H], fp32 weighted
+                             // (streaming) or bf16 (tiled)
 };
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s);
-hipError_t launch_fill_zero(float* p, size_t words, hipStream_t s);
 
-// Tile constants the host needs for grids and counters.
+// Tile constants the host needs for grids and the dispatch report.
 constexpr int kTiledBK = 64;
 constexpr int kTiledG1Features = 128;   // act columns per GEMM 1 tile (128 gate + 128 up rows)
 constexpr int kTiledG2Features = 256;   // output columns per GEMM 2 tile
 constexpr int kStreamG1Features = 16;   // act columns per streaming GEMM 1 tile
 constexpr int kStreamG2Features = 32;   // output columns per streaming GEMM 2 tile
 constexpr int kStreamBK = 256;          // K elements per streaming LDS slice
-constexpr int kCounterCols = 32;        // combine counters: room for one per (token, 32 columns)
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

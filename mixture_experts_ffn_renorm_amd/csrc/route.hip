@@ -28,8 +28,8 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
     float* __restrict__ zero_ptr, size_t zero_words) {
-  // Optional clearing of the combine scratch (fp32 sums + counters) for the
-  // GEMM 2 that follows on the same stream.
+  // Optional clearing of counters used by kernels that follow on the same
+  // stream.
   if (zero_ptr != nullptr) {
     const size_t nwg = (size_t)gridDim.x * gridDim.y;
     const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
@@ -109,16 +109,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t words) {
-  const size_t n4 = words >> 2;
-  const size_t stride = (size_t)gridDim.x * 256;
-  u32x4 z = {0u, 0u, 0u, 0u};
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
-    reinterpret_cast<u32x4*>(p)[i] = z;
-  for (size_t i = (n4 << 2) + (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += stride)
-    p[i] = 0.0f;
-}
-
 }  // namespace
 
 namespace moe_host {
@@ -143,15 +133,6 @@ hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div_host(a.M, 4));
   hipLaunchKernelGGL(route_topk_kernel, grid, dim3(256), 0, s, a.logits, a.M, a.E, a.top_k,
                      a.renormalize, a.topk_ids, a.topk_weights);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(float* p, size_t words, hipStream_t s) {
-  if (words == 0) return hipSuccess;
-  size_t blocks = (words / 4 + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
-  if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, words);
   return hipGetLastError();
 }
 

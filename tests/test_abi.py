@@ -52,9 +52,10 @@ def test_tile_table():
     assert moe.moe_pick_block_m(64, 128, 8) == 16
     assert moe.moe_pick_block_m(16, 60, 4) == 16
     assert moe.moe_pick_block_m(512, 60, 4) == 64
-    assert moe.moe_pick_block_m(2048, 60, 4) == 128
-    assert moe.moe_pick_block_m(4096, 128, 8) == 128
-    assert moe.moe_pick_block_m(8192, 256, 8) == 128
+    assert moe.moe_pick_block_m(1024, 60, 4) == 128
+    assert moe.moe_pick_block_m(2048, 60, 4) == 256
+    assert moe.moe_pick_block_m(4096, 128, 8) == 256
+    assert moe.moe_pick_block_m(8192, 256, 8) == 256
     assert moe.moe_pick_block_m(8, 256, 8) == 16
 
 

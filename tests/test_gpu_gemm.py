@@ -1,7 +1,7 @@
 """GPU parity of the two grouped GEMMs, teacher-forced: the GPU kernels get
 the oracle's routing and index lists, so each GEMM is checked on its own
 (both the weight-streaming kernels, block_m = 16, and the tiled kernels,
-block_m = 64 / 128)."""
+block_m = 64 / 128 / 256)."""
 
 from __future__ import annotations
 
@@ -72,7 +72,7 @@ MID = [dict(M=70, E=6, top_k=2, H=520, I=200, seed=31),
        dict(M=3, E=4, top_k=2, H=64, I=32, seed=34)]
 
 
-@pytest.mark.parametrize("B", [16, 64, 128])
+@pytest.mark.parametrize("B", [16, 64, 128, 256])
 @pytest.mark.parametrize("case", MID, ids=lambda c: f"M{c['M']}E{c['E']}H{c['H']}I{c['I']}")
 def test_gemms_mid_shapes(case, B):
     lay = wl.make_layer("qwen15", case["M"], E=case["E"], top_k=case["top_k"], H=case["H"],
@@ -89,7 +89,8 @@ def test_gemms_renormalize_off(B):
 
 @pytest.mark.parametrize("name,M,B", [("qwen3_decode", 64, 16), ("qwen15", 16, 16),
                                       ("qwen15", 512, 64), ("wide256", 8, 16),
-                                      ("qwen3_decode", 64, 64)])
+                                      ("qwen3_decode", 64, 64), ("qwen15", 512, 256),
+                                      ("qwen3_prefill", 4096, 256)])
 def test_gemms_full_shapes(name, M, B):
     lay = wl.make_layer(name, M)
     run_case(lay, B, pairs_checked=512)

@@ -61,7 +61,7 @@ def test_align_patterns(pattern, M, k, E):
     if k > E:
         pytest.skip("top_k > E")
     ids = wl.make_topk_ids(M, k, E, seed=1000 + M + E, pattern=pattern)
-    for B in (1, 4, 16, 32, 64, 128):
+    for B in (1, 4, 16, 32, 64, 128, 256):
         check_align(ids, E, B)
 
 
