@@ -134,13 +134,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   };
 
   // ---- per-lane copy sources of the tile being issued ----
-  int wchunk[C::kWGroups], xchunk[C::kXGroups];
-#pragma unroll
-  for (int i = 0; i < C::kWGroups; ++i) wchunk[i] = lpos ^ swz((wv + kWaves * i) * 8 + lrow);
-#pragma unroll
-  for (int i = 0; i < C::kXGroups; ++i) xchunk[i] = lpos ^ swz((wv + kWaves * i) * 8 + lrow);
+  // src: the next 16 bytes this lane copies; step: elements to advance per
+  // stage (0 for rows outside the operands, which read the zeroed page).
+  // Only the last stage of a K with a tail checks k against K.
   const uint16_t* wsrc[C::kWGroups];
   const uint16_t* xsrc[C::kXGroups];
+  int wstep[C::kWGroups], xstep[C::kXGroups];
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroPage);
+  const bool k_tail = (K % kBK) != 0;
 
   // Point the copy sources at tile i (its metadata is in LDS), and start the
   // metadata copies of tile i + 2.
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
         const int h = nt * kBN + R;
         if (h < prm.H) row = prm.w + ((size_t)e * prm.H + h) * K;
       }
-      wsrc[gi] = row;
+      wsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
+      wstep[gi] = row != nullptr ? kBK : 0;
     }
 #pragma unroll
     for (int gi = 0; gi < C::kXGroups; ++gi) {
@@ -171,31 +173,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
       if (p < P)
         row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * prm.H
                      : prm.a_src + (size_t)p * prm.I;
-      xsrc[gi] = row;
+      xsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
+      xstep[gi] = row != nullptr ? kBK : 0;
     }
     issue_meta(i + 2);
   };
 
   int is_i = 0, is_kt = 0, is_slot = 0;
-  auto issue_stage = [&](int g) {
-    const int i = is_i, kt = is_kt;
-    if (kt == 0) setup(i);
+  auto issue_stage = [&]() {
+    const int kt = is_kt;
+    if (kt == 0) setup(is_i);
     uint8_t* sb = ring + is_slot * C::kStageBytes;
     is_slot = is_slot == kStages - 1 ? 0 : is_slot + 1;
     if (++is_kt == nk) { is_kt = 0; ++is_i; }
+    // the K tail: chunks at or past K copy zeros (K is a multiple of 8)
+    const bool tail = k_tail && kt == nk - 1;
+    const int kend = K - kt * kBK;   // valid elements of this stage's 64
 #pragma unroll
     for (int gi = 0; gi < C::kWGroups; ++gi) {
-      const int k = kt * kBK + wchunk[gi] * 8;
-      const void* src = (wsrc[gi] != nullptr && k < K) ? (const void*)(wsrc[gi] + k)
-                                                        : (const void*)kZeroPage;
+      const uint16_t* src = wsrc[gi];
+      if (tail && (lpos ^ swz((wv + kWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
       load_lds16(src, sb + (wv + kWaves * gi) * 8 * kRowBytes);
+      wsrc[gi] += wstep[gi];
     }
 #pragma unroll
     for (int gi = 0; gi < C::kXGroups; ++gi) {
-      const int k = kt * kBK + xchunk[gi] * 8;
-      const void* src = (xsrc[gi] != nullptr && k < K) ? (const void*)(xsrc[gi] + k)
-                                                        : (const void*)kZeroPage;
+      const uint16_t* src = xsrc[gi];
+      if (tail && (lpos ^ swz((wv + kWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
       load_lds16(src, sb + (kBN + (wv + kWaves * gi) * 8) * kRowBytes);
+      xsrc[gi] += xstep[gi];
     }
   };
 
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < kStages - 1; ++g)
-    if (g < G) issue_stage(g);
+    if (g < G) issue_stage();
 
   bool active = true;   // this wave's half of the block holds a pair
   // One stage of MFMAs over the first NA B tiles, fully unrolled.
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     if (kStages == 3 && g + 1 < G) wait_vmem<C::kLoads>(); else wait_vmem<0>();
     // Every wave's part of stage g is in LDS, and stage g-1 is consumed.
     barrier_nofence();
-    if (g + kStages - 1 < G) issue_stage(g + kStages - 1);
+    if (g + kStages - 1 < G) issue_stage();
     const int i_tile = c_i, kt = c_kt;
     const int buf = c_buf;
     if (kt == 0) {
