@@ -17,14 +17,11 @@ constexpr int kTokTile = 16;     // tokens per MFMA tile (B columns)
 // g = l / 16) loads elements k0 + 8 g .. + 7 of its row for the 32-element
 // k step at k0, so the four lanes of a row read 64 contiguous bytes.
 //
-// kSplitK = true  (small batches): a workgroup owns 16 tokens x 16 experts
-//   and its 4 waves split K in four contiguous ranges; partial tiles are
-//   added through LDS.  Many workgroups read W_r in parallel.
-// kSplitK = false (large batches): a workgroup owns 16 tokens x 64 experts,
-//   wave w the 16 experts 16 w .. 16 w + 15 over the whole K.
-// grid: (ceil(M / 16), ceil(E / experts per workgroup)); block: 256.
-template <bool kSplitK>
-__global__ __launch_bounds__(256) void route_logits_kernel(
+// Small batches: a workgroup owns 16 tokens x 16 experts and its 4 waves
+// split K in four contiguous ranges; partial tiles are added through LDS.
+// Many workgroups read W_r in parallel.
+// grid: (ceil(M / 16), ceil(E / 16)); block: 256.
+__global__ __launch_bounds__(256) void route_logits_small_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
     float* __restrict__ zero_ptr, size_t zero_words) {
@@ -44,42 +41,33 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kTokTile;
-  const int e0 = kSplitK ? blockIdx.y * 16 : blockIdx.y * 64 + w * 16;
+  const int e0 = blockIdx.y * 16;
   const int erow = e0 + r, trow = t0 + r;
   const bool e_ok = erow < E, t_ok = trow < M;
   const uint16_t* ap = wr + (size_t)(e_ok ? erow : 0) * H;
   const uint16_t* bp = x + (size_t)(t_ok ? trow : 0) * H;
-  int kbeg = 0, kend = H;
-  if (kSplitK) {
-    const int kw = ceil_div(ceil_div(H, 4), 32) * 32;
-    kbeg = min(H, w * kw);
-    kend = min(H, kbeg + kw);
-  }
+  const int kw = ceil_div(ceil_div(H, 4), 32) * 32;
+  const int kbeg = min(H, w * kw);
+  const int kend = min(H, kbeg + kw);
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (!kSplitK && e0 >= E) {
-    // no experts for this wave
-  } else {
-    constexpr int U = kSplitK ? 16 : 8;   // k steps whose loads are in flight together
-    for (int k0 = kbeg; k0 < kend; k0 += 32 * U) {
-      u32x4 av[U], bv[U];
+  constexpr int U = 16;   // k steps whose loads are in flight together
+  for (int k0 = kbeg; k0 < kend; k0 += 32 * U) {
+    u32x4 av[U], bv[U];
 #pragma unroll
-      for (int s = 0; s < U; ++s) {
-        const int k = k0 + 32 * s + 8 * g;
-        const bool kin = k < kend;   // kend is H or a multiple of 32; H % 8 == 0
-        av[s] = load16_or_zero(ap + k, e_ok && kin);
-        bv[s] = load16_or_zero(bp + k, t_ok && kin);
-      }
-#pragma unroll
-      for (int s = 0; s < U; ++s) acc = mfma_16x16x32(av[s], bv[s], acc);
+    for (int s = 0; s < U; ++s) {
+      const int k = k0 + 32 * s + 8 * g;
+      const bool kin = k < kend;   // kend is H or a multiple of 32; H % 8 == 0
+      av[s] = load16_or_zero(ap + k, e_ok && kin);
+      bv[s] = load16_or_zero(bp + k, t_ok && kin);
     }
+#pragma unroll
+    for (int s = 0; s < U; ++s) acc = mfma_16x16x32(av[s], bv[s], acc);
   }
-  if (kSplitK) {
-    red[w][lane] = acc;
-    __syncthreads();
-    if (w != 0) return;
-    acc = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  acc = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
   // C: lane holds experts e0 + 4g + q (q = 0..3) for token t0 + r.
   if (t_ok) {
 #pragma unroll
@@ -91,6 +79,113 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
         logits[(size_t)trow * E + e] = v;
       }
     }
+  }
+}
+
+// Router logits for large batches: LDS-tiled MFMA GEMM over a tile of BT
+// tokens (32 or 64) x 128 experts, 4 waves (2 expert halves x 2 token
+// halves, each 64 experts x BT/2 tokens).  K goes through LDS in stages of
+// 64 elements, three deep, copied with global_load_lds_dwordx4; rows are
+// 128 bytes with chunk c of row R at slot c ^ ((R >> 1) & 7) (conflict-free
+// operand reads).  Expert rows and token rows past the ends, and the K
+// tail, copy a zeroed page.  Each W_r tile is read by M/BT workgroups and
+// each token row by E/128, all other reuse comes from LDS.
+constexpr int kRtBK = 64;
+constexpr int kRtStages = 3;
+constexpr int kRtExperts = 128;
+
+__device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
+
+template <int BT>
+__global__ __launch_bounds__(256) void route_logits_tiled_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
+    float* __restrict__ zero_ptr, size_t zero_words) {
+  constexpr int kRows = kRtExperts + BT;
+  constexpr int kStageBytes = kRows * 128;
+  constexpr int kCopies = kRows / 8 / 4;     // 1 KB copies per wave per stage
+  constexpr int NTB = BT / 32;               // 16-token MFMA tiles per wave
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  if (zero_ptr != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+    for (size_t i = threadIdx.x; i < zero_words; i += 256) zero_ptr[i] = 0.0f;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * kRtExperts;
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroPage);
+  // copy sources: rows 0..127 experts, 128.. tokens
+  const uint16_t* src[kCopies];
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) {
+    const int R = (wv * kCopies + c) * 8 + lrow;
+    const uint16_t* row = nullptr;
+    if (R < kRtExperts) {
+      if (e0 + R < E) row = wr + (size_t)(e0 + R) * H;
+    } else if (t0 + R - kRtExperts < M) {
+      row = x + (size_t)(t0 + R - kRtExperts) * H;
+    }
+    src[c] = row != nullptr ? row + (lpos ^ rt_swz(R)) * 8 : nullptr;
+  }
+  const int nk = ceil_div(H, kRtBK);
+  auto issue = [&](int kt) {
+    uint8_t* sb = lds + (kt % kRtStages) * kStageBytes;
+    const int kend = H - kt * kRtBK;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+      const int R = (wv * kCopies + c) * 8 + lrow;
+      const uint16_t* p = (src[c] != nullptr && (lpos ^ rt_swz(R)) * 8 < kend)
+                              ? src[c] + kt * kRtBK : zero;
+      load_lds16(p, sb + (wv * kCopies + c) * 1024);
+    }
+  };
+
+  const int we = (wv & 1) * 64, wt = (wv >> 1) * (BT / 2);
+  const int r16 = lane & 15, kg = lane >> 4;
+  int abase[2], bbase[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int slot = ((s * 4 + kg) ^ rt_swz(r16)) << 4;
+    abase[s] = (we + r16) * 128 + slot;
+    bbase[s] = (kRtExperts + wt + r16) * 128 + slot;
+  }
+  f32x4 acc[4][NTB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) wait_vmem<kCopies>(); else wait_vmem<0>();
+    barrier_nofence();
+    if (kt + 2 < nk) issue(kt + 2);
+    const uint8_t* sb = lds + (kt % kRtStages) * kStageBytes;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 af[4], bfr[NTB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + i * 16 * 128);
+#pragma unroll
+      for (int j = 0; j < NTB; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] + j * 16 * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+  }
+  // C: lane holds experts e0 + we + 16 i + 4 kg + q for token t0 + wt + 16 j + r16.
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const int t = t0 + wt + 16 * j + r16;
+    if (t >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + we + 16 * i + 4 * kg + q;
+        if (e < E) logits[(size_t)t * E + e] = acc[i][j][q] + (bias != nullptr ? bias[e] : 0.f);
+      }
   }
 }
 
@@ -113,18 +208,37 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
 namespace moe_host {
 
-// Small batches split K over the waves (more workgroups read W_r at once).
-constexpr int kSplitKMaxTokens = 256;
+// Small batches split K over the waves (more workgroups read W_r at once);
+// larger ones use the LDS-tiled kernel.
+constexpr int kSmallMaxTokens = 256;
 
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
-  if (a.M <= kSplitKMaxTokens) {
+  if (a.M <= kSmallMaxTokens) {
     dim3 grid(ceil_div_host(a.M, kTokTile), ceil_div_host(a.E, 16));
-    hipLaunchKernelGGL(route_logits_kernel<true>, grid, dim3(256), 0, s, a.x, a.w_router,
+    hipLaunchKernelGGL(route_logits_small_kernel, grid, dim3(256), 0, s, a.x, a.w_router,
                        a.bias, a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
   } else {
-    dim3 grid(ceil_div_host(a.M, kTokTile), ceil_div_host(a.E, 64));
-    hipLaunchKernelGGL(route_logits_kernel<false>, grid, dim3(256), 0, s, a.x, a.w_router,
-                       a.bias, a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
+    // 64-token tiles when they give one workgroup per CU or more, else 32
+    const int ne = ceil_div_host(a.E, kRtExperts);
+    static bool attr_set = false;   // idempotent; racing first calls set the same value
+    if (!attr_set) {
+      hipError_t err = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&route_logits_tiled_kernel<64>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, kRtStages * (kRtExperts + 64) * 128);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+    if ((long long)ceil_div_host(a.M, 64) * ne >= device_cu_count()) {
+      dim3 grid(ceil_div_host(a.M, 64), ne);
+      hipLaunchKernelGGL(route_logits_tiled_kernel<64>, grid, dim3(256),
+                         kRtStages * (kRtExperts + 64) * 128, s, a.x, a.w_router, a.bias, a.M, a.H,
+                         a.E, a.logits, a.zero_ptr, a.zero_words);
+    } else {
+      dim3 grid(ceil_div_host(a.M, 32), ne);
+      hipLaunchKernelGGL(route_logits_tiled_kernel<32>, grid, dim3(256),
+                         kRtStages * (kRtExperts + 32) * 128, s, a.x, a.w_router, a.bias, a.M, a.H,
+                         a.E, a.logits, a.zero_ptr, a.zero_words);
+    }
   }
   return hipGetLastError();
 }

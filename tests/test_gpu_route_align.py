@@ -140,6 +140,14 @@ def test_route_workloads(name, M):
     check_route(lay)
 
 
+@pytest.mark.parametrize("M,E,k,H", [(300, 60, 4, 520), (777, 200, 8, 1032), (2100, 6, 2, 64)])
+def test_route_large_batch_ragged(M, E, k, H):
+    """Batches above 256 tokens take the LDS-tiled router GEMM: partial token
+    and expert tiles and a K tail (H not a multiple of 64)."""
+    lay = wl.make_layer("qwen15", M, E=E, top_k=k, H=H, I=8, seed=M + E)
+    check_route(lay)
+
+
 def test_route_no_renormalize():
     check_route(wl.make_layer("qwen15", 512, I=8), renormalize=False)
     check_route(wl.make_layer("toy", 3), renormalize=False)
