@@ -22,8 +22,8 @@
 // operand, so each lane ends with 4 consecutive features of one pair.  With
 // BM = 256 an expert of up to 256 pairs reads each weight tile once, and
 // each k step of LDS operands feeds twice the MFMAs of BM = 128 (measured:
-// about 1.3x the rate).  A wave group whose half of the block holds only
-// pads (the tail of an expert's last block) skips its MFMAs.
+// about 1.3x the rate).  Quarters of the block that hold only pads (the
+// tail of an expert's last block) skip their MFMAs.
 //
 // Persistent workgroups, one per CU.  Each XCD owns a contiguous range of
 // tiles (block-major, all column tiles of a block side by side) and its
@@ -208,23 +208,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   // ---- this wave's MFMA tiles ----
   // A tiles (weight rows): GEMM 1 gate rows wf*32 + {0, 16} and the matching
   // up rows kHalf + wf*32 + {0, 16}; GEMM 2 rows wf*64 + {0, 16, 32, 48}.
-  // B tiles (pairs): rows wp * BM/2 + 16 j, j < NT: the wave group wp owns
-  // one half of the block, and skips its MFMAs when that half holds only
-  // pads (the tail of an expert's last block); the two waves that share a
-  // SIMD own different halves, so a half-empty block takes about half the
-  // time.  Every tile starts at a multiple of 16 rows, so a lane's swizzle
-  // depends only on r16 and each tile's offset is a constant added to one
-  // base per operand and k half.
+  // B tiles (pairs): the block's pairs are four quarters of BM/4; wave
+  // group wp owns quarters wp and wp + 2 (B tiles j < NT/2 and j >= NT/2),
+  // and skips the MFMAs of a quarter that holds only pads (the tail of an
+  // expert's last block).  The four waves of a group sit on the four SIMDs,
+  // so a block with one quarter of pairs takes about a quarter of the time.
+  // Every tile starts at a multiple of 16 rows, so a lane's swizzle depends
+  // only on r16 and each tile's offset is a constant added to one base per
+  // operand and k half.
+  constexpr int QS = BM / 4, TQ = NT / 2;   // pairs and B tiles per quarter
   const int wf = wv % C::kWF, wp = wv / C::kWF;
   const int r16 = lane & 15, kg = lane >> 4;
-  auto brow = [&](int j) { return wp * (BM / 2) + 16 * j; };   // first pair of B tile j
+  auto brow = [&](int j) { return (j < TQ ? wp : wp + 2) * QS + 16 * (j % TQ); };
   const int arow0 = kGemm1 ? wf * 32 : wf * 64;
   int abase[2], bbase[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int slot = ((s * 4 + kg) ^ swz(r16)) << 4;
     abase[s] = (arow0 + r16) * kRowBytes + slot;
-    bbase[s] = (kBN + wp * (BM / 2) + r16) * kRowBytes + slot;
+    bbase[s] = (kBN + wp * QS + r16) * kRowBytes + slot;
   }
   auto aconst = [](int i) {
     return (kGemm1 ? (i >> 1) * kHalf + (i & 1) * 16 : 16 * i) * kRowBytes;
@@ -245,23 +247,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   for (int g = 0; g < kStages - 1; ++g)
     if (g < G) issue_stage();
 
-  bool active = true;   // this wave's half of the block holds a pair
-  // One stage of MFMAs over the first NA B tiles, fully unrolled.
-  auto compute = [&](auto na, const uint8_t* sb) {
-    constexpr int NA = decltype(na)::value;
+  bool act0 = true, act1 = true;   // this wave's quarters hold a pair
+  // One stage of MFMAs over this wave's active quarters, fully unrolled.
+  auto compute = [&](const uint8_t* sb) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4 af[4], bfr[NA > 0 ? NA : 1];
+      u32x4 af[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + aconst(i));
 #pragma unroll
-      for (int j = 0; j < NA; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] + j * 16 * kRowBytes);
+      for (int q = 0; q < 2; ++q) {
+        if (!(q == 0 ? act0 : act1)) continue;
+        u32x4 bfr[TQ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < TQ; ++j)
+          bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] +
+                                                   (q * 2 * QS + 16 * j) * kRowBytes);
 #pragma unroll
-        for (int j = 0; j < NA; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < TQ; ++j)
+            acc[i][q * TQ + j] = mfma_16x16x32(af[i], bfr[j], acc[i][q * TQ + j]);
+      }
     }
   };
   int c_i = 0, c_kt = 0, c_buf = 0, c_slot = 0;
@@ -274,13 +282,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     const int i_tile = c_i, kt = c_kt;
     const int buf = c_buf;
     if (kt == 0) {
-      bool any = false;
-#pragma unroll
-      for (int r = lane; r < BM / 2; r += 64) any |= s_pair[buf][wp * (BM / 2) + r] < P;
-      active = __ballot(any) != 0ull;
+      const bool v0 = lane < QS && s_pair[buf][wp * QS + lane] < P;
+      const bool v1 = lane < QS && s_pair[buf][(wp + 2) * QS + lane] < P;
+      act0 = __ballot(v0) != 0ull;
+      act1 = __ballot(v1) != 0ull;
     }
     const uint8_t* sb = ring + c_slot * C::kStageBytes;
-    if (active) compute(std::integral_constant<int, NT>{}, sb);
+    if (act0 || act1) compute(sb);
     c_slot = c_slot == kStages - 1 ? 0 : c_slot + 1;
     if (++c_kt == nk) { c_kt = 0; ++c_i; c_buf = c_buf == kMeta - 1 ? 0 : c_buf + 1; }
     if (kt != nk - 1) continue;
@@ -288,9 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     // ---- tile epilogue: lane holds features 4*kg + q of each A tile, pair r16 of each B tile ----
     const int jt = j0 + i_tile * nslots;
     const int nt = jt - (jt / ntn) * ntn;
-    if (!active) continue;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
+      if (!(j < TQ ? act0 : act1)) continue;
       const int p = s_pair[buf][brow(j) + r16];
       if (p < P) {
         if (kGemm1) {
