@@ -71,6 +71,8 @@ typedef struct moe_dispatch_info {
   int block_k;   /* K elements per pipeline step                                 */
   int k_tail;    /* 1 if some K (H for GEMM 1, I for GEMM 2) is not a multiple of block_k */
   int launches;  /* kernels this call queued                                     */
+  int sorted;    /* moe_forward: 1 = pairs sorted by expert; 0 = one block per pair
+                    (M*top_k*4 <= E: small batches skip the sort)                */
 } moe_dispatch_info;
 
 /* Bytes of workspace that moe_forward needs for any M <= M_max with these

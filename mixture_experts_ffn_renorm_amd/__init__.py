@@ -36,7 +36,8 @@ class MoeError(RuntimeError):
 
 class DispatchInfo(ctypes.Structure):
     _fields_ = [("variant", _c_int), ("block_m", _c_int), ("block_n", _c_int),
-                ("block_k", _c_int), ("k_tail", _c_int), ("launches", _c_int)]
+                ("block_k", _c_int), ("k_tail", _c_int), ("launches", _c_int),
+                ("sorted", _c_int)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

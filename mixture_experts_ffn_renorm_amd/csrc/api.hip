@@ -79,11 +79,19 @@ bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // Small batches run the top-k and the index lists in one launch.
 bool fused_route(int M, int top_k) { return align_segments(M * top_k) == 1; }
 
+// Very small batches skip the sort (page "Mixture of Experts in vLLM ...",
+// sub-section "Small batches skip the sort"): one block per pair when
+// M*top_k*4 <= E, with the weight-streaming kernels.
+bool per_pair_blocks(int M, int top_k, int E, int B) {
+  return B == 16 && (long long)M * top_k * 4 <= E;
+}
+
 // Kernels queued by one GEMM 2 call: the GEMM and the per-token weighted sum.
 constexpr int kGemm2Launches = 2;
 
-void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches) {
+void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches, int sorted = 1) {
   if (info == nullptr) return;
+  info->sorted = sorted;
   const bool stream = B == 16;
   info->variant = stream ? MOE_VARIANT_STREAM : MOE_VARIANT_TILED;
   info->block_m = B;
@@ -278,7 +286,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
-  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches);
+  const bool per_pair = per_pair_blocks(M, top_k, E, B);
+  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches, per_pair ? 0 : 1);
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
   if (!a16(x) || !a16(w_router) || !a16(w13) || !a16(w2) || !a16(out) || !a16(workspace))
@@ -303,7 +312,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
                reinterpret_cast<int32_t*>(ws + L.align_scratch)};
   MOE_TRY_HIP(launch_route_logits(ra, s));
   if (fused_route(M, top_k)) {
-    MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive), s));
+    MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive),
+                                        per_pair, s));
   } else {
     MOE_TRY_HIP(launch_route_topk(ra, s));
     MOE_TRY_HIP(launch_align(aa, s));

@@ -329,9 +329,11 @@ int align_segments(int P);
 size_t align_scratch_bytes(int P, int E);
 hipError_t launch_align(const AlignArgs& a, hipStream_t s);
 // Top-k of all tokens and the index lists in one launch (one align segment);
-// arrivals: one int, zero before the launch.
+// arrivals: one int, zero before the launch.  per_pair: the small-batch
+// form of the lists (block p = pair p alone, expert_ids = the top-k ids,
+// expert_block_offsets[E] = P; the other offsets and counts are not written).
 hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32_t* arrivals,
-                                   hipStream_t s);
+                                   bool per_pair, hipStream_t s);
 
 struct GemmArgs {
   const uint16_t* a_src;     // GEMM 1: x [M, H]; GEMM 2: act [P, I]

@@ -52,7 +52,7 @@ def check_forward(lay: dict, n_tokens: int = 256, seed: int = 0, **kw):
     return info, out
 
 
-FORWARD_CASES = [("toy", 3)] + [("qwen3_decode", m) for m in (1, 2, 8, 16, 64)] + \
+FORWARD_CASES = [("toy", 3)] + [("qwen3_decode", m) for m in (1, 2, 4, 8, 16, 64)] + \
     [("qwen3_prefill", 4096)] + [("qwen15", m) for m in (1, 16, 512, 2048)] + \
     [("wide256", m) for m in (1, 8, 8192)]
 
@@ -71,6 +71,8 @@ def test_forward_workloads(name, M):
         assert info["variant"] == moe.MOE_VARIANT_TILED
     bk = info["block_k"]
     assert info["k_tail"] == int(lay["H"] % bk != 0 or lay["I"] % bk != 0)
+    # small batches skip the sort (one block per pair) when M*top_k*4 <= E
+    assert info["sorted"] == int(not (B == 16 and M * lay["top_k"] * 4 <= lay["E"]))
     if name == "qwen15" and B == 16:
         assert info["k_tail"] == 1       # I = 1408 is not a multiple of 256
 
