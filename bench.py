@@ -38,6 +38,9 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 DEFAULT_WORKLOAD = ("qwen3_decode", 64)
 
 
+VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv"}
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +219,8 @@ def main():
                for j, n in enumerate(names)}
 
     work = algorithmic(shape, M, mean_touched)
+    # the staged C-ABI calls always build index lists; the forward itself may
+    # run the per-pair GEMVs instead (reported as forward_variant)
     variant = "stream" if B == 16 else "tiled"
     # dominant kernel: GEMM 1 (2/3 of the weight bytes and of the flops)
     mfma_bound = variant == "tiled" and work["gemm1_flops"] / work["gemm1_bytes"] > \
@@ -252,6 +257,7 @@ def main():
         "config": {"workload": name, "description": shape.description, "M": M, "E": E,
                    "top_k": k, "H": H, "I": I, "renormalize": shape.renormalize,
                    "layers_cycled": L, "block_m": B, "variant": variant,
+                   "forward_variant": VARIANT_NAMES[info["variant"]],
                    "mean_touched_experts": mean_touched},
         "layer": {"alg_bytes": int(work["layer_bytes"]), "alg_flops": int(work["layer_flops"]),
                   "hbm_frac": round(work["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -268,8 +274,8 @@ def main():
             outs = torch.empty((Ms, H), dtype=torch.bfloat16, device=dev)
             for i in range(args.warmup):
                 lay = layers[i % L]
-                moe.moe_forward(xs, lay["w_router"], lay["w13"], lay["w2"], k, True,
-                                out=outs, ws=ws, stream=stream)
+                _, sinfo = moe.moe_forward(xs, lay["w_router"], lay["w13"], lay["w2"], k, True,
+                                           out=outs, ws=ws, stream=stream)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for i in range(args.steps):
@@ -278,7 +284,8 @@ def main():
                                 out=outs, ws=ws, stream=stream)
             torch.cuda.synchronize()
             dt = (time.perf_counter() - t0) / args.steps
-            sweep[f"M={Ms}"] = {"tokens_per_s": round(Ms / dt, 1), "us_per_layer": round(1e6 * dt, 2)}
+            sweep[f"M={Ms}"] = {"tokens_per_s": round(Ms / dt, 1), "us_per_layer": round(1e6 * dt, 2),
+                                "variant": VARIANT_NAMES[sinfo["variant"]]}
         result["decode_sweep"] = sweep
 
     # ---- the oracle on the host, on a bounded sample ----

@@ -64,6 +64,8 @@ typedef enum moe_status {
  * timing. */
 #define MOE_VARIANT_TILED 0   /* LDS-tiled MFMA grouped GEMM (many rows per expert) */
 #define MOE_VARIANT_STREAM 1  /* weight-streaming MFMA kernel (about one row per expert) */
+#define MOE_VARIANT_PAIR_GEMV 2  /* moe_forward only: per-pair GEMVs, no index lists
+                                    (M*top_k*4 <= E: small batches skip the sort) */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -71,8 +73,8 @@ typedef struct moe_dispatch_info {
   int block_k;   /* K elements per pipeline step                                 */
   int k_tail;    /* 1 if some K (H for GEMM 1, I for GEMM 2) is not a multiple of block_k */
   int launches;  /* kernels this call queued                                     */
-  int sorted;    /* moe_forward: 1 = pairs sorted by expert; 0 = one block per pair
-                    (M*top_k*4 <= E: small batches skip the sort)                */
+  int sorted;    /* moe_forward: 1 = pairs sorted by expert into index lists;
+                    0 = no lists, one GEMV per pair (MOE_VARIANT_PAIR_GEMV)      */
 } moe_dispatch_info;
 
 /* Bytes of workspace that moe_forward needs for any M <= M_max with these
@@ -174,7 +176,7 @@ int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
  *   topk_weights [M*top_k] fp32
  *   out          out [M, H] bf16 in token order
  *   workspace    holds the pair-order product [M*top_k, H] (block_m 16:
- *                fp32, already scaled by topk_weights; 64 and 128: bf16,
+ *                fp32, already scaled by topk_weights; 64, 128, 256: bf16,
  *                scaled in the sum), ws_bytes >= moe_workspace_size(M, E,
  *                top_k, H, I)
  * A second kernel adds each token's top_k rows in slot order in fp32 and
@@ -195,6 +197,11 @@ int moe_grouped_gemm_w2_combine(const uint16_t* act, const uint16_t* w2,
  * across layers (page "MoE Execution Path Analysis", "Memory allocation per
  * step" and "What we can actually change"); block_m comes from
  * moe_pick_block_m (the same page's per-batch-size BLOCK_SIZE_M choice).
+ * Very small batches, M*top_k*4 <= E, build no index lists: each pair runs
+ * as its own GEMV against its expert's weights, read from the top-k ids
+ * (page "Mixture of Experts in vLLM ...", sub-section "Small batches skip
+ * the sort"), and GEMM 2 sums the weighted rows per token in the same
+ * launch; info->variant then reads MOE_VARIANT_PAIR_GEMV, info->sorted 0.
  *
  *   x [M, H], w_router [E, H], w13 [E, 2I, H], w2 [E, H, I]: bf16
  *   logit_bias       [E] fp32 or NULL

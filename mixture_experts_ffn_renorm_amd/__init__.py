@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
 
 MOE_VARIANT_TILED = 0
 MOE_VARIANT_STREAM = 1
+MOE_VARIANT_PAIR_GEMV = 2
 
 _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int

@@ -228,15 +228,12 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
 // stores, waits for them, and counts its arrival in *arrivals (zeroed by the
 // router-logits kernel on the same stream); the last one reads all P ids
 // back with agent-coherent loads.  A lone workgroup keeps its ids in LDS.
-// per_pair (page "Mixture of Experts in vLLM ...", sub-section "Small
-// batches skip the sort"): when M*top_k*4 <= E there is no sort; block p
-// holds pair p alone (the rest of it pads) and its expert is topk_ids[p].
 __global__ __launch_bounds__(kThreads) void route_topk_align_kernel(
     const float* __restrict__ logits, int M, int E, int top_k, int renormalize, int B,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
     int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
     int32_t* __restrict__ boff_out, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ arrivals, int per_pair) {
+    int32_t* __restrict__ arrivals) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int s_last;
   const int P = M * top_k;
@@ -252,17 +249,7 @@ __global__ __launch_bounds__(kThreads) void route_topk_align_kernel(
       __hip_atomic_store(topk_ids + p, r.id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       topk_weights[p] = r.w;
       ids_lds[p] = r.id;
-      if (per_pair) {
-        // small batches skip the sort: block p holds pair p alone
-        expert_ids[p] = r.id;
-        sorted[p * B] = (int)p;
-        for (int j = 1; j < B; ++j) sorted[p * B + j] = P;
-      }
     }
-  }
-  if (per_pair) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) boff_out[E] = P;   // the block count
-    return;
   }
   if (gridDim.x > 1) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -290,7 +277,7 @@ constexpr size_t kFusedRouteMaxLds = route_topk_align_lds(kAlignPairsPerSegment,
 static_assert(kFusedRouteMaxLds <= 100 * 1024, "fused top-k + align LDS");
 
 hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32_t* arrivals,
-                                   bool per_pair, hipStream_t s) {
+                                   hipStream_t s) {
   const size_t lds = route_topk_align_lds(r.M * r.top_k, r.E);
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
@@ -303,7 +290,7 @@ hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32
   hipLaunchKernelGGL(route_topk_align_kernel, dim3(ceil_div_host(r.M, kTopkWaves)), dim3(kThreads),
                      lds, s, r.logits, r.M, r.E, r.top_k, r.renormalize, a.block_m, r.topk_ids,
                      r.topk_weights, a.sorted_token_ids, a.expert_ids, a.expert_block_offsets,
-                     a.expert_counts, arrivals, per_pair ? 1 : 0);
+                     a.expert_counts, arrivals);
   return hipGetLastError();
 }
 

@@ -80,18 +80,31 @@ bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool fused_route(int M, int top_k) { return align_segments(M * top_k) == 1; }
 
 // Very small batches skip the sort (page "Mixture of Experts in vLLM ...",
-// sub-section "Small batches skip the sort"): one block per pair when
-// M*top_k*4 <= E, with the weight-streaming kernels.
-bool per_pair_blocks(int M, int top_k, int E, int B) {
-  return B == 16 && (long long)M * top_k * 4 <= E;
-}
+// sub-section "Small batches skip the sort"): when M*top_k*4 <= E every pair
+// is its own product, run as per-pair GEMVs that read topk_ids directly.
+bool per_pair_gemv(int M, int top_k, int E) { return (long long)M * top_k * 4 <= E; }
 
 // Kernels queued by one GEMM 2 call: the GEMM and the per-token weighted sum.
 constexpr int kGemm2Launches = 2;
 
-void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches, int sorted = 1) {
+// Kernels queued by moe_forward's per-pair path: router logits, top-k,
+// GEMV 1, GEMV 2 with the weighted sum.
+constexpr int kPairGemvForwardLaunches = 4;
+
+void fill_info_pair_gemv(moe_dispatch_info* info, int H, int I) {
   if (info == nullptr) return;
-  info->sorted = sorted;
+  info->sorted = 0;
+  info->variant = MOE_VARIANT_PAIR_GEMV;
+  info->block_m = 1;
+  info->block_n = kPairGemvFeatures;
+  info->block_k = kPairGemvK;
+  info->k_tail = (H % kPairGemvK != 0 || I % kPairGemvK != 0) ? 1 : 0;
+  info->launches = kPairGemvForwardLaunches;
+}
+
+void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches) {
+  if (info == nullptr) return;
+  info->sorted = 1;
   const bool stream = B == 16;
   info->variant = stream ? MOE_VARIANT_STREAM : MOE_VARIANT_TILED;
   info->block_m = B;
@@ -286,8 +299,11 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
-  const bool per_pair = per_pair_blocks(M, top_k, E, B);
-  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches, per_pair ? 0 : 1);
+  const bool per_pair = M > 0 && per_pair_gemv(M, top_k, E);
+  if (per_pair)
+    fill_info_pair_gemv(info, H, I);
+  else
+    fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches);
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
   if (!a16(x) || !a16(w_router) || !a16(w13) || !a16(w2) || !a16(out) || !a16(workspace))
@@ -311,9 +327,15 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
                reinterpret_cast<int32_t*>(ws + L.counts),
                reinterpret_cast<int32_t*>(ws + L.align_scratch)};
   MOE_TRY_HIP(launch_route_logits(ra, s));
+  if (per_pair) {
+    PairGemvArgs pg{x, w13, w2, ids, wts, M, top_k, H, I, act, out};
+    MOE_TRY_HIP(launch_route_topk(ra, s));
+    MOE_TRY_HIP(launch_pair_gemv1(pg, s));
+    MOE_TRY_HIP(launch_pair_gemv2(pg, s));
+    return MOE_OK;
+  }
   if (fused_route(M, top_k)) {
-    MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive),
-                                        per_pair, s));
+    MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive), s));
   } else {
     MOE_TRY_HIP(launch_route_topk(ra, s));
     MOE_TRY_HIP(launch_align(aa, s));

@@ -329,11 +329,9 @@ int align_segments(int P);
 size_t align_scratch_bytes(int P, int E);
 hipError_t launch_align(const AlignArgs& a, hipStream_t s);
 // Top-k of all tokens and the index lists in one launch (one align segment);
-// arrivals: one int, zero before the launch.  per_pair: the small-batch
-// form of the lists (block p = pair p alone, expert_ids = the top-k ids,
-// expert_block_offsets[E] = P; the other offsets and counts are not written).
+// arrivals: one int, zero before the launch.
 hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32_t* arrivals,
-                                   bool per_pair, hipStream_t s);
+                                   hipStream_t s);
 
 struct GemmArgs {
   const uint16_t* a_src;     // GEMM 1: x [M, H]; GEMM 2: act [P, I]
@@ -352,6 +350,22 @@ hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s);
 
+// Per-pair GEMVs of very small batches (no index lists): GEMM 1 writes
+// act [P, I]; GEMM 2 multiplies, weights and sums each token's top_k rows
+// straight into out [M, H].
+struct PairGemvArgs {
+  const uint16_t* x;          // [M, H]
+  const uint16_t* w13;        // [E, 2I, H]
+  const uint16_t* w2;         // [E, H, I]
+  const int32_t* topk_ids;    // [M, top_k]
+  const float* topk_weights;  // [M, top_k]
+  int M, top_k, H, I;
+  uint16_t* act;              // [M*top_k, I]
+  uint16_t* out;              // [M, H]
+};
+hipError_t launch_pair_gemv1(const PairGemvArgs& a, hipStream_t s);
+hipError_t launch_pair_gemv2(const PairGemvArgs& a, hipStream_t s);
+
 // Tile constants the host needs for grids and the dispatch report.
 constexpr int kTiledBK = 64;
 constexpr int kTiledG1Features = 128;   // act columns per GEMM 1 tile (128 gate + 128 up rows)
@@ -359,6 +373,8 @@ constexpr int kTiledG2Features = 256;   // output columns per GEMM 2 tile
 constexpr int kStreamG1Features = 16;   // act columns per streaming GEMM 1 tile
 constexpr int kStreamG2Features = 32;   // output columns per streaming GEMM 2 tile
 constexpr int kStreamBK = 256;          // K elements per streaming LDS slice
+constexpr int kPairGemvFeatures = 16;   // act columns per per-pair GEMV 1 workgroup
+constexpr int kPairGemvK = 2048;        // K elements per lane-pass of the per-pair GEMVs
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -62,19 +62,56 @@ def test_forward_workloads(name, M):
     moe = _moe()
     lay = wl.make_layer(name, M)
     info, _ = check_forward(lay)
-    B = moe.moe_pick_block_m(M, lay["E"], lay["top_k"])
-    assert info["block_m"] == B
-    assert info["variant"] == (moe.MOE_VARIANT_STREAM if B == 16 else moe.MOE_VARIANT_TILED)
-    if name in ("qwen3_decode",) or (name, M) in (("wide256", 1), ("wide256", 8)):
+    check_dispatch(lay, info)
+    if (name, M) in (("qwen3_decode", 1), ("qwen3_decode", 4), ("wide256", 1), ("wide256", 8),
+                     ("qwen15", 1)):
+        assert info["variant"] == moe.MOE_VARIANT_PAIR_GEMV
+    if (name, M) in (("qwen3_decode", 8), ("qwen3_decode", 64), ("qwen15", 16)):
         assert info["variant"] == moe.MOE_VARIANT_STREAM
     if (name, M) in (("qwen3_prefill", 4096), ("wide256", 8192)):
         assert info["variant"] == moe.MOE_VARIANT_TILED
+    if name == "qwen15" and info["block_m"] == 16:
+        assert info["k_tail"] == 1       # I = 1408 is not a multiple of 256
+
+
+def check_dispatch(lay: dict, info: dict):
+    """What moe_forward reports it ran: small batches (M*top_k*4 <= E) skip
+    the sort and run per-pair GEMVs (four launches, no index lists); the
+    others use the tile table's block size."""
+    moe = _moe()
+    M, E, k = lay["M"], lay["E"], lay["top_k"]
+    if M * k * 4 <= E:
+        assert info["variant"] == moe.MOE_VARIANT_PAIR_GEMV
+        assert info["sorted"] == 0 and info["block_m"] == 1 and info["launches"] == 4
+    else:
+        B = moe.moe_pick_block_m(M, E, k)
+        assert info["block_m"] == B and info["sorted"] == 1
+        assert info["variant"] == (moe.MOE_VARIANT_STREAM if B == 16 else moe.MOE_VARIANT_TILED)
     bk = info["block_k"]
     assert info["k_tail"] == int(lay["H"] % bk != 0 or lay["I"] % bk != 0)
-    # small batches skip the sort (one block per pair) when M*top_k*4 <= E
-    assert info["sorted"] == int(not (B == 16 and M * lay["top_k"] * 4 <= lay["E"]))
-    if name == "qwen15" and B == 16:
-        assert info["k_tail"] == 1       # I = 1408 is not a multiple of 256
+
+
+# Per-pair GEMV shapes beyond the workloads: K over several 2048-element
+# passes with a ragged last pass (H = 4104), I not a multiple of the 16
+# features of a GEMM 1 workgroup, top_k above the 8 waves of GEMM 2 (slots
+# loop), the largest top_k, and top_k = 1.
+PAIR_GEMV_CASES = [
+    dict(M=2, E=64, top_k=2, H=4104, I=520, seed=21),
+    dict(M=2, E=128, top_k=12, H=256, I=136, seed=22),
+    dict(M=1, E=512, top_k=32, H=1032, I=64, seed=23),
+    dict(M=3, E=16, top_k=1, H=64, I=32, seed=24),
+    dict(M=4, E=32, top_k=2, H=2048, I=1416, seed=25),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_GEMV_CASES, ids=lambda c: "M{M}_E{E}_k{top_k}_H{H}_I{I}".format(**c))
+def test_forward_pair_gemv_shapes(case):
+    c = dict(case)
+    M = c.pop("M")
+    lay = wl.make_layer("toy", M, **c)
+    info, _ = check_forward(lay)
+    check_dispatch(lay, info)
+    assert info["variant"] == _moe().MOE_VARIANT_PAIR_GEMV
 
 
 @pytest.mark.parametrize("M", [16, 64])
@@ -149,12 +186,14 @@ def test_forward_zero_tokens():
     assert out.shape == (0, 64) and info["launches"] == 0
 
 
-def test_forward_poisoned_workspace_and_guard_bands():
+@pytest.mark.parametrize("M", [16, 2])
+def test_forward_poisoned_workspace_and_guard_bands(M):
     """Workspace filled with NaN bytes before the call; output rows written
-    through a view with canary rows on both sides."""
+    through a view with canary rows on both sides (sorted path and per-pair
+    GEMVs)."""
     import torch
     moe = _moe()
-    lay = wl.make_layer("qwen3_decode", 16)
+    lay = wl.make_layer("qwen3_decode", M)
     M, H = lay["M"], lay["H"]
     ws = moe.workspace(M, lay["E"], lay["top_k"], H, lay["I"])
     ws.fill_(0xFF)
