@@ -350,8 +350,8 @@ hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s);
 
-// Per-pair GEMVs of very small batches (no index lists): GEMM 1 writes
-// act [P, I]; GEMM 2 multiplies, weights and sums each token's top_k rows
+// Per-pair GEMVs of very small batches (no index lists): GEMV 1 writes
+// act [P, I]; GEMV 2 multiplies, weights and sums each token's top_k rows
 // straight into out [M, H].
 struct PairGemvArgs {
   const uint16_t* x;          // [M, H]

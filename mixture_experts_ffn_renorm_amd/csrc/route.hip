@@ -82,6 +82,64 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(
   }
 }
 
+// Router logits for very small batches (M <= 16), GEMV-style: wave w of
+// workgroup (bx, by) owns expert e = 4 bx + w and tokens 4 by .. 4 by + 3.
+// Lane l takes the 16-byte chunks l, l + 64, ... of the W_r row and of the
+// token rows (NC per lane per pass of 512 NC elements), all loads of a pass
+// in flight together; fp32 products of the exact bf16 values, one wave sum
+// per token.  Many workgroups (one per 4 experts) read W_r at once.
+constexpr int kGemvTokens = 4;
+
+template <int NC>
+__global__ __launch_bounds__(256) void route_logits_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
+    float* __restrict__ zero_ptr, size_t zero_words) {
+  if (zero_ptr != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+    for (size_t i = threadIdx.x; i < zero_words; i += 256) zero_ptr[i] = 0.0f;
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;   // whole wave; no barrier follows
+  const int t0 = blockIdx.y * kGemvTokens;
+  const int nchunk = H / 8;
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(wr + (size_t)e * H);
+  const u32x4* xrow[kGemvTokens];
+#pragma unroll
+  for (int u = 0; u < kGemvTokens; ++u)
+    xrow[u] = reinterpret_cast<const u32x4*>(x + (size_t)(t0 + u < M ? t0 + u : 0) * H);
+  float acc[kGemvTokens];
+#pragma unroll
+  for (int u = 0; u < kGemvTokens; ++u) acc[u] = 0.f;
+  for (int base = lane; base < nchunk + lane; base += 64 * NC) {
+    u32x4 wv[NC], xv[kGemvTokens][NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = base + 64 * c;
+      wv[c] = load16_or_zero(wrow + (ch < nchunk ? ch : 0), ch < nchunk);
+#pragma unroll
+      for (int u = 0; u < kGemvTokens; ++u)
+        xv[u][c] = load16_or_zero(xrow[u] + (ch < nchunk ? ch : 0), ch < nchunk);
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvTokens; ++u)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[u] = __builtin_fmaf(__uint_as_float(wv[c][q] << 16),
+                                  __uint_as_float(xv[u][c][q] << 16), acc[u]);
+          acc[u] = __builtin_fmaf(__uint_as_float(wv[c][q] & 0xffff0000u),
+                                  __uint_as_float(xv[u][c][q] & 0xffff0000u), acc[u]);
+        }
+  }
+  const float b = bias != nullptr ? bias[e] : 0.f;
+#pragma unroll
+  for (int u = 0; u < kGemvTokens; ++u) {
+    const float v = wave_sum(acc[u]);
+    if (lane == 0 && t0 + u < M) logits[(size_t)(t0 + u) * E + e] = v + b;
+  }
+}
+
 // Router logits for large batches: LDS-tiled MFMA GEMM over a tile of BT
 // tokens (32 or 64) x 128 experts, 4 waves (2 expert halves x 2 token
 // halves, each 64 experts x BT/2 tokens).  K goes through LDS in stages of
@@ -212,8 +270,26 @@ namespace moe_host {
 // larger ones use the LDS-tiled kernel.
 constexpr int kSmallMaxTokens = 256;
 
+// Batches up to this many tokens use the GEMV-style kernel.
+constexpr int kGemvMaxTokens = 16;
+
+template <int NC>
+void launch_route_gemv(const RouteArgs& a, hipStream_t s) {
+  dim3 grid(ceil_div_host(a.E, 4), ceil_div_host(a.M, kGemvTokens));
+  hipLaunchKernelGGL(route_logits_gemv_kernel<NC>, grid, dim3(256), 0, s, a.x, a.w_router, a.bias,
+                     a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
+}
+
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
-  if (a.M <= kSmallMaxTokens) {
+  if (a.M <= kGemvMaxTokens) {
+    const int n = (a.H / 8 + 63) / 64;   // chunks per lane covering H, at most 4 per pass
+    switch (n <= 1 ? 1 : (n >= 4 ? 4 : n)) {
+      case 1: launch_route_gemv<1>(a, s); break;
+      case 2: launch_route_gemv<2>(a, s); break;
+      case 3: launch_route_gemv<3>(a, s); break;
+      default: launch_route_gemv<4>(a, s); break;
+    }
+  } else if (a.M <= kSmallMaxTokens) {
     dim3 grid(ceil_div_host(a.M, kTokTile), ceil_div_host(a.E, 16));
     hipLaunchKernelGGL(route_logits_small_kernel, grid, dim3(256), 0, s, a.x, a.w_router,
                        a.bias, a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
