@@ -178,50 +178,66 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_s = M * args.steps / elapsed
 
-    # ---- per-kernel times: the same work as separate C-ABI calls with HIP
-    #      events between them on the launch stream ----
+    # ---- per-kernel times: the same work as separate C-ABI calls, one step
+    #      at a time: each call is launched `steps` times back to back (layer
+    #      i % L, with that layer's own routing and index lists) between two
+    #      HIP events on the launch stream, so event overhead is amortised ----
     B = moe.moe_pick_block_m(M, E, k)
     cap, nbl = moe.align_capacity(M * k, E, B)
-    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
-    eids = torch.empty(max(nbl, 1), dtype=torch.int32, device=dev)
-    boff = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
     act = torch.empty((M * k, I), dtype=torch.bfloat16, device=dev)
     logits = torch.empty((M, E), dtype=torch.float32, device=dev)
     align_ws = torch.empty(max(moe.moe_align_workspace_size(M, k, E), 16), dtype=torch.uint8,
                            device=dev)
-    names = ["route", "align", "gemm1", "gemm2"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-
-    def staged(i, ev=None):
-        lay = layers[i % L]
-        if ev: ev[0].record(stream)
+    routed = []
+    for i in range(L):
+        lay = layers[i]
+        r_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+        r_wts = torch.empty((M, k), dtype=torch.float32, device=dev)
         moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
-                      topk_ids=ids, topk_weights=wts, logits_out=logits, stream=stream)
-        if ev: ev[1].record(stream)
-        moe.moe_align(ids, E, B, sorted_ids, eids, boff, counts, ws=align_ws, stream=stream)
-        if ev: ev[2].record(stream)
-        moe.moe_grouped_gemm_w13_act(x, lay["w13"], sorted_ids, eids, boff, k, B, act=act,
-                                     stream=stream)
-        if ev: ev[3].record(stream)
-        moe.moe_grouped_gemm_w2_combine(act, lay["w2"], wts, sorted_ids, eids, boff, M, k, B,
-                                        out=out, ws=ws, stream=stream)
-        if ev: ev[4].record(stream)
+                      topk_ids=r_ids, topk_weights=r_wts, logits_out=logits, stream=stream)
+        lists = (torch.empty(cap, dtype=torch.int32, device=dev),
+                 torch.empty(max(nbl, 1), dtype=torch.int32, device=dev),
+                 torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 torch.empty(E, dtype=torch.int32, device=dev))
+        moe.moe_align(r_ids, E, B, *lists, ws=align_ws, stream=stream)
+        routed.append((r_ids, r_wts, lists))
+    scratch_lists = tuple(torch.empty_like(t) for t in routed[0][2])
 
-    for i in range(min(args.warmup, 10)):
-        staged(i)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        staged(i, evs[i])
-    torch.cuda.synchronize()
-    kern_us = {n: 1e3 * float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
-                                        for i in range(args.steps)]))
-               for j, n in enumerate(names)}
+    def stage(name, i):
+        lay = layers[i % L]
+        r_ids, r_wts, (s_ids, e_ids, b_off, cnt) = routed[i % L]
+        if name == "route":
+            moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
+                          topk_ids=ids, topk_weights=wts, logits_out=logits, stream=stream)
+        elif name == "align":
+            moe.moe_align(r_ids, E, B, *scratch_lists, ws=align_ws, stream=stream)
+        elif name == "gemm1":
+            moe.moe_grouped_gemm_w13_act(x, lay["w13"], s_ids, e_ids, b_off, k, B, act=act,
+                                         stream=stream)
+        else:
+            moe.moe_grouped_gemm_w2_combine(act, lay["w2"], r_wts, s_ids, e_ids, b_off, M, k, B,
+                                            out=out, ws=ws, stream=stream)
+
+    names = ["route", "align", "gemm1", "gemm2"]
+    kern_us = {}
+    for n in names:
+        for i in range(min(args.warmup, 10)):
+            stage(n, i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            stage(n, i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern_us[n] = 1e3 * e0.elapsed_time(e1) / args.steps
 
     work = algorithmic(shape, M, mean_touched)
-    # the staged C-ABI calls always build index lists; the forward itself may
-    # run the per-pair GEMVs instead (reported as forward_variant)
-    variant = "stream" if B == 16 else "tiled"
+    # the staged calls run the forward's kernel family at the same block size;
+    # at block_m 1 GEMM 1 is the forward's own GEMV (in index-list order),
+    # while the forward's GEMM 2 reads topk_ids and sums in the same launch
+    variant = {1: "pair_gemv", 16: "stream"}.get(B, "tiled")
     # dominant kernel: GEMM 1 (2/3 of the weight bytes and of the flops)
     mfma_bound = variant == "tiled" and work["gemm1_flops"] / work["gemm1_bytes"] > \
         1e3 * BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 0.5

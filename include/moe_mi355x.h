@@ -64,8 +64,8 @@ typedef enum moe_status {
  * timing. */
 #define MOE_VARIANT_TILED 0   /* LDS-tiled MFMA grouped GEMM (many rows per expert) */
 #define MOE_VARIANT_STREAM 1  /* weight-streaming MFMA kernel (about one row per expert) */
-#define MOE_VARIANT_PAIR_GEMV 2  /* moe_forward only: per-pair GEMVs, no index lists
-                                    (M*top_k*4 <= E: small batches skip the sort) */
+#define MOE_VARIANT_PAIR_GEMV 2  /* per-pair GEMVs (block_m 1; moe_forward uses them,
+                                    with no index lists, when M*top_k*4 <= E) */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -86,9 +86,9 @@ size_t moe_workspace_size(int M_max, int E, int top_k, int H, int I);
 const char* moe_strerror(int status);
 
 /* The block size (block_m) moe_forward uses for a batch of M tokens: the
- * compiled tile table, keyed on the mean number of pairs per expert
- * (M*top_k/E).  Returns 16 (weight-streaming kernels), 64, 128 or 256
- * (tiled). */
+ * compiled tile table.  Returns 1 (per-pair GEMVs) when M >= 1 and
+ * M*top_k*4 <= E; otherwise, keyed on the mean number of pairs per expert
+ * (M*top_k/E), 16 (weight-streaming kernels), 64, 128 or 256 (tiled). */
 int moe_pick_block_m(int M, int E, int top_k);
 
 /*
@@ -152,8 +152,10 @@ int moe_align(const int32_t* topk_ids, int M, int top_k, int E, int block_m,
  * by row).  The [M*top_k, 2I] GEMM 1 output never exists in memory.
  *
  *   x      [M, H] bf16;  w13 [E, 2I, H] bf16 (gate rows first)
- *   index lists from moe_align with the same block_m (16, 64, 128 or 256;
- *   16 selects the weight-streaming kernel, the others the tiled kernel)
+ *   index lists from moe_align with the same block_m (1, 16, 64, 128 or
+ *   256; 1 selects the per-pair GEMV, one pair per block, which reads its
+ *   expert's weights once per pair and suits only very small batches; 16
+ *   the weight-streaming kernel; the others the tiled kernel)
  *   act    out [M*top_k, I] bf16 in pair order (row p = t*top_k + j)
  *   info   host, optional: which kernel ran
  * Accumulation is fp32; act is rounded to bf16 once.
@@ -175,10 +177,10 @@ int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
  *   w2           [E, H, I] bf16
  *   topk_weights [M*top_k] fp32
  *   out          out [M, H] bf16 in token order
- *   workspace    holds the pair-order product [M*top_k, H] (block_m 16:
- *                fp32, already scaled by topk_weights; 64, 128, 256: bf16,
- *                scaled in the sum), ws_bytes >= moe_workspace_size(M, E,
- *                top_k, H, I)
+ *   workspace    holds the pair-order product [M*top_k, H] (block_m 1 and
+ *                16: fp32, already scaled by topk_weights; 64, 128, 256:
+ *                bf16, scaled in the sum), ws_bytes >= moe_workspace_size(M,
+ *                E, top_k, H, I)
  * A second kernel adds each token's top_k rows in slot order in fp32 and
  * rounds once to bf16, so results are bitwise repeatable.
  */

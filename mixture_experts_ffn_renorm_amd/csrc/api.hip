@@ -64,9 +64,9 @@ int check_sizes(int M, int E, int top_k, int H, int I) {
   return MOE_OK;
 }
 
-// Block sizes the GEMM calls accept (16: weight-streaming kernels; the
-// others: tiled kernels).
-constexpr int kBlockSizes[] = {16, 64, 128, 256};
+// Block sizes the GEMM calls accept (1: per-pair GEMVs; 16: weight-streaming
+// kernels; the others: tiled kernels).
+constexpr int kBlockSizes[] = {1, 16, 64, 128, 256};
 bool gemm_block_ok(int B) {
   for (int b : kBlockSizes)
     if (B == b) return true;
@@ -81,8 +81,11 @@ bool fused_route(int M, int top_k) { return align_segments(M * top_k) == 1; }
 
 // Very small batches skip the sort (page "Mixture of Experts in vLLM ...",
 // sub-section "Small batches skip the sort"): when M*top_k*4 <= E every pair
-// is its own product, run as per-pair GEMVs that read topk_ids directly.
-bool per_pair_gemv(int M, int top_k, int E) { return (long long)M * top_k * 4 <= E; }
+// is its own product, run as per-pair GEMVs (block_m 1); moe_forward then
+// builds no index lists and the GEMVs read topk_ids directly.
+bool per_pair_gemv(int M, int top_k, int E) {
+  return M >= 1 && (long long)M * top_k * 4 <= E;
+}
 
 // Kernels queued by one GEMM 2 call: the GEMM and the per-token weighted sum.
 constexpr int kGemm2Launches = 2;
@@ -91,25 +94,20 @@ constexpr int kGemm2Launches = 2;
 // GEMV 1, GEMV 2 with the weighted sum.
 constexpr int kPairGemvForwardLaunches = 4;
 
-void fill_info_pair_gemv(moe_dispatch_info* info, int H, int I) {
+void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches, int sorted = 1) {
   if (info == nullptr) return;
-  info->sorted = 0;
-  info->variant = MOE_VARIANT_PAIR_GEMV;
-  info->block_m = 1;
-  info->block_n = kPairGemvFeatures;
-  info->block_k = kPairGemvK;
-  info->k_tail = (H % kPairGemvK != 0 || I % kPairGemvK != 0) ? 1 : 0;
-  info->launches = kPairGemvForwardLaunches;
-}
-
-void fill_info(moe_dispatch_info* info, int B, int H, int I, int launches) {
-  if (info == nullptr) return;
-  info->sorted = 1;
-  const bool stream = B == 16;
-  info->variant = stream ? MOE_VARIANT_STREAM : MOE_VARIANT_TILED;
+  info->sorted = sorted;
   info->block_m = B;
-  info->block_n = stream ? kStreamG1Features : kTiledG1Features;
-  info->block_k = stream ? kStreamBK : kTiledBK;
+  if (B == 1) {
+    info->variant = MOE_VARIANT_PAIR_GEMV;
+    info->block_n = kPairGemvFeatures;
+    info->block_k = kPairGemvK;
+  } else {
+    const bool stream = B == 16;
+    info->variant = stream ? MOE_VARIANT_STREAM : MOE_VARIANT_TILED;
+    info->block_n = stream ? kStreamG1Features : kTiledG1Features;
+    info->block_k = stream ? kStreamBK : kTiledBK;
+  }
   info->k_tail = (H % info->block_k != 0 || I % info->block_k != 0) ? 1 : 0;
   info->launches = launches;
 }
@@ -131,12 +129,42 @@ GemmArgs gemm_args(int M, int top_k, int E, int H, int I, int B) {
   return g;
 }
 
+// block_m 1: the per-pair GEMVs in index-list order (one pair per block).
+PairGemvArgs pair_args(const GemmArgs& g) {
+  PairGemvArgs a{};
+  a.M = g.M;
+  a.top_k = g.top_k;
+  a.H = g.H;
+  a.I = g.I;
+  a.sorted = g.sorted_token_ids;
+  a.expert_ids = g.expert_ids;
+  a.topk_weights = g.topk_weights;
+  return a;
+}
+
 int run_gemm1(GemmArgs g, hipStream_t s) {
+  if (g.block_m == 1) {
+    PairGemvArgs a = pair_args(g);
+    a.x = g.a_src;
+    a.w13 = g.w;
+    a.act = g.out;
+    MOE_TRY_HIP(launch_pair_gemv1(a, s));
+    return MOE_OK;
+  }
   MOE_TRY_HIP(g.block_m == 16 ? launch_gemm1_stream(g, s) : launch_gemm1_tiled(g, s));
   return MOE_OK;
 }
 
 int run_gemm2(GemmArgs g, hipStream_t s) {
+  if (g.block_m == 1) {
+    PairGemvArgs a = pair_args(g);
+    a.act = const_cast<uint16_t*>(g.a_src);
+    a.w2 = g.w;
+    a.out = g.out;
+    a.partial = g.partial;
+    MOE_TRY_HIP(launch_pair_gemv2(a, s));
+    return MOE_OK;
+  }
   MOE_TRY_HIP(g.block_m == 16 ? launch_gemm2_stream(g, s) : launch_gemm2_tiled(g, s));
   return MOE_OK;
 }
@@ -183,6 +211,7 @@ const char* moe_strerror(int status) {
 
 int moe_pick_block_m(int M, int E, int top_k) {
   if (E <= 0) return 16;
+  if (per_pair_gemv(M, top_k, E)) return 1;
   const double per_expert = (double)M * top_k / E;
   if (per_expert <= 8.0) return 16;
   if (per_expert <= 48.0) return 64;
@@ -299,9 +328,9 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
   const int B = moe_pick_block_m(M, E, top_k);
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
-  const bool per_pair = M > 0 && per_pair_gemv(M, top_k, E);
+  const bool per_pair = B == 1;
   if (per_pair)
-    fill_info_pair_gemv(info, H, I);
+    fill_info(info, B, H, I, kPairGemvForwardLaunches, 0);
   else
     fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches);
   if (M == 0) return MOE_OK;
@@ -328,7 +357,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
                reinterpret_cast<int32_t*>(ws + L.align_scratch)};
   MOE_TRY_HIP(launch_route_logits(ra, s));
   if (per_pair) {
-    PairGemvArgs pg{x, w13, w2, ids, wts, M, top_k, H, I, act, out};
+    PairGemvArgs pg{x, w13, w2, ids, wts, M, top_k, H, I, act, out, nullptr, nullptr, nullptr};
     MOE_TRY_HIP(launch_route_topk(ra, s));
     MOE_TRY_HIP(launch_pair_gemv1(pg, s));
     MOE_TRY_HIP(launch_pair_gemv2(pg, s));

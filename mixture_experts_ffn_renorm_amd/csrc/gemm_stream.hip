@@ -396,9 +396,14 @@ hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s) {
                      ring2::kRingBytes, s, prm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long n4 = (long long)a.M * (a.H / 4);
+  return launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
+}
+
+hipError_t launch_combine_partials(const float* partial, int M, int top_k, int H, uint16_t* out,
+                                   hipStream_t s) {
+  const long long n4 = (long long)M * (H / 4);
   hipLaunchKernelGGL(ring2::combine_partials_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256),
-                     0, s, a.partial, a.M, a.top_k, a.H, a.out);
+                     0, s, partial, M, top_k, H, out);
   return hipGetLastError();
 }
 

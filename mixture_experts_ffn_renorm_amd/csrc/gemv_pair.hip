@@ -12,6 +12,12 @@
 // token's row held in registers in the same chunk order, and a wave
 // reduction gives each dot product.
 //
+// The per-step GEMM calls reach the same kernels with block_m 1: index lists
+// of one pair per block (no pads), block b holding pair sorted[b] of expert
+// expert_ids[b]; GEMV 1 is the same kernel in that order, and GEMV 2 then
+// writes fp32 rows of pair p, already scaled by topk_weights[p], for the
+// per-token sum kernel (it has no topk_ids to group a token's pairs).
+//
 // GEMV 1 (sub-section "One GEMM 1 program, step by step", one pair per
 //   program): a workgroup owns one pair p and 4*FW act columns, wave w the FW
 //   columns f0 = (4 blockIdx.x + w) FW ..: gate rows f of W13[e] and the
@@ -62,16 +68,20 @@ __device__ __forceinline__ u32x4 chunk_or_zero(const uint16_t* row, int chunk, i
 }
 
 // NC = 16-byte chunks per lane per pass: one pass covers 512*NC elements of K.
+// Block b = blockIdx.y: pair p = b and expert ids[p] (ids = topk_ids), or,
+// with index lists, pair sorted[b] and expert ids[b] (ids = expert_ids).
 template <int NC, int FW>
 __global__ __launch_bounds__(64 * kG1Waves) void gemv_w13_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
-    const int32_t* __restrict__ topk_ids, int top_k, int H, int I, uint16_t* __restrict__ act) {
-  const int p = blockIdx.y;
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ ids, int top_k, int H, int I,
+    uint16_t* __restrict__ act) {
+  const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int f0 = (blockIdx.x * kG1Waves + (threadIdx.x >> 6)) * FW;
   // I % 8 == 0 and FW divides 8: a wave's columns are all valid or all past I
   if (f0 >= I) return;   // whole wave; no barrier follows
-  const int e = topk_ids[p];
+  const int p = sorted != nullptr ? sorted[b] : b;
+  const int e = ids[b];
   const int nchunk = H / 8;
   const uint16_t* xrow = x + (size_t)(p / top_k) * H;
   const uint16_t* gate = w13 + ((size_t)e * 2 * I + f0) * H;   // rows f0 ..
@@ -153,6 +163,49 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_w2_sum_kernel(
   }
 }
 
+// GEMV 2, index-list form: block b = blockIdx.y holds pair p = sorted[b] of
+// expert expert_ids[b]; wave w of the workgroup owns output columns
+// h0 = 8 blockIdx.x + 2w and h0 + 1 and writes
+// partial[p, h] = topk_weights[p] * (W2[e][h] . act[p]) in fp32.
+template <int NC>
+__global__ __launch_bounds__(256) void gemv_w2_rows_kernel(
+    const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ expert_ids,
+    const float* __restrict__ topk_weights, int H, int I, float* __restrict__ partial) {
+  constexpr int R = 2;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int h0 = blockIdx.x * 8 + (threadIdx.x >> 6) * R;   // H % 8 == 0: all rows exist
+  const int p = sorted[b];
+  const int e = expert_ids[b];
+  const int nchunk = I / 8;
+  const uint16_t* arow = act + (size_t)p * I;
+  const uint16_t* wrow = w2 + ((size_t)e * H + h0) * I;
+  float s[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) s[r] = 0.f;
+  for (int base = lane; base < nchunk + lane; base += 64 * NC) {
+    u32x4 av[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) av[c] = chunk_or_zero<false>(arow, base + 64 * c, nchunk);
+    u32x4 wv[R][NC];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        wv[r][c] = chunk_or_zero<true>(wrow + (size_t)r * I, base + 64 * c, nchunk);
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = dot_chunks<NC>(wv[r], av, s[r]);
+  }
+  const float wt = topk_weights[p];
+#pragma unroll
+  for (int r = 0; r < R; ++r) s[r] = wave_sum(s[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) partial[(size_t)p * H + h0 + r] = wt * s[r];
+  }
+}
+
 // Chunks per lane per pass for a K of k elements: enough to cover K in one
 // pass up to 2048, then passes of 2048.
 int chunks_per_lane(int k) {
@@ -165,8 +218,16 @@ int waves_for(int top_k) { return top_k < kMaxWaves ? top_k : kMaxWaves; }
 template <int NC>
 void launch_w13(const moe_host::PairGemvArgs& a, hipStream_t s) {
   dim3 grid(moe_host::ceil_div_host(a.I, kG1Waves * kG1Cols), a.M * a.top_k);
+  const int32_t* ids = a.sorted != nullptr ? a.expert_ids : a.topk_ids;
   hipLaunchKernelGGL((gemv_w13_kernel<NC, kG1Cols>), grid, dim3(64 * kG1Waves), 0, s, a.x, a.w13,
-                     a.topk_ids, a.top_k, a.H, a.I, a.act);
+                     a.sorted, ids, a.top_k, a.H, a.I, a.act);
+}
+
+template <int NC>
+void launch_w2_rows(const moe_host::PairGemvArgs& a, hipStream_t s) {
+  dim3 grid(a.H / 8, a.M * a.top_k);
+  hipLaunchKernelGGL(gemv_w2_rows_kernel<NC>, grid, dim3(256), 0, s, a.act, a.w2, a.sorted,
+                     a.expert_ids, a.topk_weights, a.H, a.I, a.partial);
 }
 
 template <int NC>
@@ -191,6 +252,17 @@ hipError_t launch_pair_gemv1(const PairGemvArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pair_gemv2(const PairGemvArgs& a, hipStream_t s) {
+  if (a.sorted != nullptr) {
+    switch (chunks_per_lane(a.I)) {
+      case 1: launch_w2_rows<1>(a, s); break;
+      case 2: launch_w2_rows<2>(a, s); break;
+      case 3: launch_w2_rows<3>(a, s); break;
+      default: launch_w2_rows<4>(a, s); break;
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
+  }
   switch (chunks_per_lane(a.I)) {
     case 1: launch_w2<1>(a, s); break;
     case 2: launch_w2<2>(a, s); break;

@@ -349,19 +349,27 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s);
+// out[t] = bf16(sum over slots j of partial[t*top_k + j]), j ascending.
+hipError_t launch_combine_partials(const float* partial, int M, int top_k, int H, uint16_t* out,
+                                   hipStream_t s);
 
-// Per-pair GEMVs of very small batches (no index lists): GEMV 1 writes
-// act [P, I]; GEMV 2 multiplies, weights and sums each token's top_k rows
-// straight into out [M, H].
+// Per-pair GEMVs of very small batches: GEMV 1 writes act [P, I]; GEMV 2
+// multiplies, weights and sums each token's top_k rows straight into
+// out [M, H] (sorted == null: pair p's expert is topk_ids[p]), or, with
+// index lists of one pair per block (sorted, expert_ids from block_m 1),
+// writes weighted fp32 rows to partial [P, H] and queues the per-token sum.
 struct PairGemvArgs {
   const uint16_t* x;          // [M, H]
   const uint16_t* w13;        // [E, 2I, H]
   const uint16_t* w2;         // [E, H, I]
-  const int32_t* topk_ids;    // [M, top_k]
+  const int32_t* topk_ids;    // [M, top_k] (no lists)
   const float* topk_weights;  // [M, top_k]
   int M, top_k, H, I;
   uint16_t* act;              // [M*top_k, I]
   uint16_t* out;              // [M, H]
+  const int32_t* sorted;      // block_m 1 lists: pair of block b, or null
+  const int32_t* expert_ids;  // block_m 1 lists: expert of block b
+  float* partial;             // [M*top_k, H] fp32 (lists form of GEMV 2)
 };
 hipError_t launch_pair_gemv1(const PairGemvArgs& a, hipStream_t s);
 hipError_t launch_pair_gemv2(const PairGemvArgs& a, hipStream_t s);
@@ -373,7 +381,7 @@ constexpr int kTiledG2Features = 256;   // output columns per GEMM 2 tile
 constexpr int kStreamG1Features = 16;   // act columns per streaming GEMM 1 tile
 constexpr int kStreamG2Features = 32;   // output columns per streaming GEMM 2 tile
 constexpr int kStreamBK = 256;          // K elements per streaming LDS slice
-constexpr int kPairGemvFeatures = 16;   // act columns per per-pair GEMV 1 workgroup
+constexpr int kPairGemvFeatures = 4;    // act columns per per-pair GEMV 1 workgroup
 constexpr int kPairGemvK = 2048;        // K elements per lane-pass of the per-pair GEMVs
 
 // Compute units of the current device (cached per device).

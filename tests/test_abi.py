@@ -48,7 +48,12 @@ def test_strerror():
 
 def test_tile_table():
     moe = _moe()
-    assert moe.moe_pick_block_m(1, 128, 8) == 16
+    # per-pair GEMVs while M*top_k*4 <= E
+    assert moe.moe_pick_block_m(1, 128, 8) == 1
+    assert moe.moe_pick_block_m(4, 128, 8) == 1
+    assert moe.moe_pick_block_m(5, 128, 8) == 16
+    assert moe.moe_pick_block_m(3, 60, 4) == 1
+    assert moe.moe_pick_block_m(0, 60, 4) == 16
     assert moe.moe_pick_block_m(64, 128, 8) == 16
     assert moe.moe_pick_block_m(16, 60, 4) == 16
     assert moe.moe_pick_block_m(512, 60, 4) == 64
@@ -56,7 +61,8 @@ def test_tile_table():
     assert moe.moe_pick_block_m(2048, 60, 4) == 256
     assert moe.moe_pick_block_m(4096, 128, 8) == 256
     assert moe.moe_pick_block_m(8192, 256, 8) == 256
-    assert moe.moe_pick_block_m(8, 256, 8) == 16
+    assert moe.moe_pick_block_m(8, 256, 8) == 1
+    assert moe.moe_pick_block_m(9, 256, 8) == 16
 
 
 def test_workspace_size_monotone_and_bounded():
@@ -121,7 +127,7 @@ def test_other_calls_argument_checks():
     assert moe.moe_align_workspace_size(4, 2, 8) == 0
     assert moe.moe_align_workspace_size(8192, 8, 256) > 0
     assert lib.moe_align(fake, 8192, 8, 256, 16, fake, fake, fake, NULL, NULL, 0, NULL) == -3
-    # GEMMs: block_m must be 16, 64 or 128
+    # GEMMs: block_m must be 1, 16, 64, 128 or 256
     assert lib.moe_grouped_gemm_w13_act(fake, fake, fake, fake, fake, 4, 2, 8, 64, 32, 32,
                                         fake, ctypes.byref(info), NULL) == -2
     assert lib.moe_grouped_gemm_w13_act(fake, fake, fake, fake, fake, 0, 2, 8, 64, 32, 16,

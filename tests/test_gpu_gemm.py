@@ -1,7 +1,7 @@
 """GPU parity of the two grouped GEMMs, teacher-forced: the GPU kernels get
 the oracle's routing and index lists, so each GEMM is checked on its own
-(both the weight-streaming kernels, block_m = 16, and the tiled kernels,
-block_m = 64 / 128 / 256)."""
+(the per-pair GEMVs, block_m = 1, the weight-streaming kernels, block_m = 16,
+and the tiled kernels, block_m = 64 / 128 / 256)."""
 
 from __future__ import annotations
 
@@ -44,7 +44,8 @@ def run_case(lay: dict, B: int, pairs_checked: int = 4096, seed: int = 0):
     # GEMM 1 + SiLU*up, pair order
     act, info = moe.moe_grouped_gemm_w13_act(d["x"], d["w13"], s, e, off, k, B)
     torch.cuda.synchronize()
-    assert info["variant"] == (moe.MOE_VARIANT_STREAM if B == 16 else moe.MOE_VARIANT_TILED)
+    variant = {1: moe.MOE_VARIANT_PAIR_GEMV, 16: moe.MOE_VARIANT_STREAM}
+    assert info["variant"] == variant.get(B, moe.MOE_VARIANT_TILED)
     toks = h.sample_tokens(M, max(1, pairs_checked // k), seed)
     ref_act = mo.pair_activations(lay["x"], lay["w13"], ids, toks)
     rows = (toks[:, None] * k + np.arange(k)).reshape(-1)
@@ -72,7 +73,7 @@ MID = [dict(M=70, E=6, top_k=2, H=520, I=200, seed=31),
        dict(M=3, E=4, top_k=2, H=64, I=32, seed=34)]
 
 
-@pytest.mark.parametrize("B", [16, 64, 128, 256])
+@pytest.mark.parametrize("B", [1, 16, 64, 128, 256])
 @pytest.mark.parametrize("case", MID, ids=lambda c: f"M{c['M']}E{c['E']}H{c['H']}I{c['I']}")
 def test_gemms_mid_shapes(case, B):
     lay = wl.make_layer("qwen15", case["M"], E=case["E"], top_k=case["top_k"], H=case["H"],
@@ -80,14 +81,16 @@ def test_gemms_mid_shapes(case, B):
     run_case(lay, B)
 
 
-@pytest.mark.parametrize("B", [16, 128])
+@pytest.mark.parametrize("B", [1, 16, 128])
 def test_gemms_renormalize_off(B):
     lay = wl.make_layer("qwen15", 40, E=8, top_k=3, H=256, I=64, seed=41)
     lay["renormalize"] = False
     run_case(lay, B)
 
 
-@pytest.mark.parametrize("name,M,B", [("qwen3_decode", 64, 16), ("qwen15", 16, 16),
+@pytest.mark.parametrize("name,M,B", [("qwen3_decode", 1, 1), ("qwen3_decode", 4, 1),
+                                      ("wide256", 8, 1), ("qwen15", 3, 1),
+                                      ("qwen3_decode", 64, 16), ("qwen15", 16, 16),
                                       ("qwen15", 512, 64), ("wide256", 8, 16),
                                       ("qwen3_decode", 64, 64), ("qwen15", 512, 256),
                                       ("qwen3_prefill", 4096, 256)])
