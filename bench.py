@@ -51,6 +51,8 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=16, help="distinct layers cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the many-layer stack (eager and HIP-graph replay) figures")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration runs)")
     return ap.parse_args()
@@ -303,6 +305,39 @@ def main():
             sweep[f"M={Ms}"] = {"tokens_per_s": round(Ms / dt, 1), "us_per_layer": round(1e6 * dt, 2),
                                 "variant": VARIANT_NAMES[sinfo["variant"]]}
         result["decode_sweep"] = sweep
+
+    # ---- the cycled layers as one model-shaped stack: layer l's output is
+    #      layer l + 1's input, one workspace, eager steps and one captured
+    #      HIP graph replayed (context figures; `value` above is the layer) ----
+    if not args.no_stack:
+        from mixture_experts_ffn_renorm_amd.stack import MoEStack
+        stack = MoEStack(layers, k, M, shape.renormalize)
+        nst = max(2, min(args.steps, 20))
+        stack.step(x)
+        torch.cuda.synchronize()
+        mem0 = torch.cuda.memory_allocated()
+        t0 = time.perf_counter()
+        for _ in range(nst):
+            stack.step(x)
+        torch.cuda.synchronize()
+        eager_s = (time.perf_counter() - t0) / nst
+        alloc_delta = torch.cuda.memory_allocated() - mem0
+        x_static = x.clone()
+        graph, _ = stack.capture(x_static)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(nst):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - t0) / nst
+        result["stack"] = {"layers": L, "launches_per_step": stack.last_launches,
+                           "device_bytes_allocated_per_step": int(alloc_delta),
+                           "us_per_layer_eager": round(1e6 * eager_s / L, 2),
+                           "us_per_layer_graph": round(1e6 * graph_s / L, 2),
+                           "layer_tokens_per_s_graph": round(M * L / graph_s, 1)}
+        del graph, stack
 
     # ---- the oracle on the host, on a bounded sample ----
     if not args.no_cpu_baseline:
