@@ -183,8 +183,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_kernel(StreamParams 
 // expert and the gathered act rows, so the copy ring keeps streaming across
 // tile boundaries and a tile's combine epilogue runs while the next tile's
 // first slices are in flight; the ring is drained only where the block
-// changes.  Epilogue: the tile (64 columns x 16 pairs) is staged in LDS and
-// stored as fp32 partial rows p = topk_weights[p] * (W2[e] act[p]); the
+// changes.  Epilogue: each lane stores its four columns of the tile (64
+// columns x 16 pairs) straight from its MFMA registers as fp32 partial rows
+// p = topk_weights[p] * (W2[e] act[p]) -- no LDS staging and no barrier, so
+// the next slices' copies keep streaming.  (Measured at 64 tokens: the
+// kernel runs ~67 us against ~59 us for the same ring streaming the same
+// bytes with no compute; dropping the 4 MB of partial-row stores recovers
+// ~5 us, while LDS staging, barriers, deferring the stores to the end of
+// the run, and streaming across block boundaries changed nothing.)  The
 // per-token sum is the small combine kernel below (at these batch sizes the
 // partial rows are a few MB, while an in-kernel last-arrival combine costs
 // each tile three serialized memory round trips).
@@ -210,7 +216,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
   __shared__ int s_pair[kBM];
   __shared__ float s_wt[kBM];
   __shared__ int s_e;
-  __shared__ float s_ct[kBM][kWRows + 1];
 
   const int P = prm.M * prm.top_k;
   const int H = prm.H, K = prm.I;
@@ -286,25 +291,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
       }
       if (g % ns != ns - 1) continue;
 
-      // ---- tile epilogue (copies of the next tile stay in flight) ----
+      // ---- tile epilogue, straight from registers (no LDS, no barrier; the
+      //      copies of the next slices stay in flight): lane holds rows
+      //      wv*16 + 4 kg + q (q = 0..3) of the tile for pair column r16 ----
       const int nt = nt0 + g / ns;
-      // lane holds rows wv*16 + 4 kg + q for pair column r16
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s_ct[r16][wv * 16 + 4 * kg + q] = acc[q];
+      const int p = s_pair[r16];
+      const int h = nt * kWRows + wv * 16 + 4 * kg;   // H % 8 == 0: all four exist or none
+      if (p < P && h < H)
+        *reinterpret_cast<f32x4*>(prm.partial + (size_t)p * H + h) = s_wt[r16] * acc;
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();
-      {
-        const int pr = tid >> 4, c4 = (tid & 15) * 4;
-        const int p = s_pair[pr];
-        const int h = nt * kWRows + c4;
-        if (p < P && h < H) {
-          f32x4 v;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = s_wt[pr] * s_ct[pr][c4 + q];
-          *reinterpret_cast<f32x4*>(prm.partial + (size_t)p * H + h) = v;
-        }
-      }
-      __syncthreads();                 // s_ct is reused by the next tile
     }
     t = run_end;
     __syncthreads();                   // s_pair / s_e are reloaded for the next block
