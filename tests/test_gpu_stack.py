@@ -126,10 +126,13 @@ def test_stack_last_layer_matches_oracle():
     h.assert_close_outputs(got[ok], ref["y"][ok], "last layer")
 
 
-@pytest.mark.parametrize("M", [2, 16])
-def test_stack_graph_replay_matches_eager(M):
+@pytest.mark.parametrize("name,M", [("qwen3_decode", 2), ("qwen3_decode", 16),
+                                    ("qwen15", 512), ("qwen15", 2048)])
+def test_stack_graph_replay_matches_eager(name, M):
+    """Per-pair GEMVs, streaming kernels with the fused top-k + lists, and the
+    tiled kernels with the multi-workgroup align (M = 2048: 8192 pairs)."""
     import torch
-    stack, shape, layers = make_stack("qwen3_decode", M, n=3)
+    stack, shape, layers = make_stack(name, M, n=3 if M <= 16 else 2)
     from mixture_experts_ffn_renorm_amd.stack import MoEStack
     ref_stack = MoEStack(layers, shape.top_k, M, shape.renormalize)
     inputs = [draw_x(M, shape.H, 20 + r) for r in range(3)]
