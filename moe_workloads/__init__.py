@@ -15,7 +15,7 @@ Shapes follow the pages this project builds from:
   * "MoE Execution Path Analysis", "The Real Bottleneck": 256 experts with
     top-8 routing (the wide layer below keeps that routing shape).
 
-Value distributions (the readings are stated in the design doc):
+Value distributions (readings of the pages where they leave details open):
   x ~ N(0, 1); W13 ~ N(0, 1/H) and W2 ~ N(0, 1/I) (variance 1/fan-in);
   W_r ~ N(0, 0.02^2) for the model-shaped layers and N(0, 1/H) for the toy.
   Every tensor is drawn in float32 and rounded once, round-to-nearest-even,
