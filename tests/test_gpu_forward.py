@@ -223,3 +223,25 @@ def test_forward_repeatable():
     assert np.array_equal(i1, i2) and np.array_equal(w1, w2)
     a, b = h.host_bf16_to_f64(o1), h.host_bf16_to_f64(o2)
     assert np.abs(a - b).max() <= 2 ** -7 * np.abs(a).max()
+
+
+# Long K in every kernel family: H = 7168 (not a multiple of 2048: the
+# per-pair GEMV 1 takes four passes, the last one ragged), I = 2048.
+# M = 1 runs the per-pair GEMVs, M = 24 the streaming kernels (6 pairs per
+# expert), M = 512 the tiled kernels (128 pairs per expert).
+@pytest.fixture(scope="module")
+def long_k_layer():
+    return wl.make_layer("toy", 512, E=16, top_k=4, H=7168, I=2048, seed=61)
+
+
+@pytest.mark.parametrize("M,variant", [(1, "pair"), (24, "stream"), (512, "tiled")])
+def test_forward_long_k(long_k_layer, M, variant):
+    moe = _moe()
+    lay = dict(long_k_layer)
+    lay["x"] = lay["x"][:M]
+    lay["M"] = M
+    info, _ = check_forward(lay, n_tokens=12, seed=5)
+    check_dispatch(lay, info)
+    want = {"pair": moe.MOE_VARIANT_PAIR_GEMV, "stream": moe.MOE_VARIANT_STREAM,
+            "tiled": moe.MOE_VARIANT_TILED}[variant]
+    assert info["variant"] == want
