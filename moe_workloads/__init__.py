@@ -223,3 +223,79 @@ def make_device_layer(shape: LayerShape | str, M: int, layer: int, device,
         rank = torch.randperm(E, generator=g, device=device).to(torch.float64) + 1
         bias = (-shape.zipf_s * torch.log(rank)).to(torch.float32)
     return dict(w_router=w_router, w13=w13, w2=w2, logit_bias=bias)
+
+
+# ---------------------------------------------------------------------------
+# group-quantized expert weights (affine, 64-element groups, 4 or 8 bits)
+# ---------------------------------------------------------------------------
+
+QUANT_GROUP = 64
+
+
+def _pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack codes [..., K] (K a multiple of 32 / bits) into uint32 words,
+    element i of a row at bits [bits * (i % per), ...) of word i // per."""
+    per = 32 // bits
+    c = np.asarray(codes, dtype=np.uint32).reshape(*codes.shape[:-1], codes.shape[-1] // per, per)
+    words = np.zeros(c.shape[:-1], dtype=np.uint32)
+    for i in range(per):
+        words |= c[..., i] << np.uint32(bits * i)
+    return words
+
+
+def _quantized_matrix(rows: int, K: int, bits: int, seq: np.random.SeedSequence):
+    """Random codes, scales and biases of one expert matrix [rows, K]: codes
+    uniform over [0, 2^bits); per 64-element group a scale and bias (bf16)
+    that map the code range onto about [-a, a] with a = sqrt(3 / K) (a
+    variance near 1/K, like the bf16 layers), each jittered by 10 %."""
+    rng = np.random.Generator(np.random.PCG64(seq))
+    codes = rng.integers(0, 1 << bits, size=(rows, K), dtype=np.uint32)
+    ng = K // QUANT_GROUP
+    a = math.sqrt(3.0 / K)
+    s = (2.0 * a / ((1 << bits) - 1)) * (1.0 + 0.1 * rng.standard_normal((rows, ng)))
+    b = -a * (1.0 + 0.1 * rng.standard_normal((rows, ng)))
+    return (_pack_codes(codes, bits), f32_to_bf16_bits(s.astype(np.float32)),
+            f32_to_bf16_bits(b.astype(np.float32)))
+
+
+def make_quantized_layer(shape: LayerShape | str, M: int, bits: int, layer: int = 0,
+                         E: Optional[int] = None, top_k: Optional[int] = None,
+                         H: Optional[int] = None, I: Optional[int] = None,
+                         seed: Optional[int] = None) -> dict:
+    """One synthetic layer with group-quantized expert weights.
+
+    x, w_router (bf16) and the Zipf prior are drawn as by :func:`make_layer`;
+    W13 [E, 2I, H] and W2 [E, H, I] come as packed codes
+    (``w13_q`` [E, 2I, H*bits/32] uint32), ``*_scales`` and ``*_biases``
+    [E, rows, K/64] (bf16 bits).  H and I must be multiples of 64.
+    """
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    E = shape.E if E is None else E
+    top_k = shape.top_k if top_k is None else top_k
+    H = shape.H if H is None else H
+    I = shape.I if I is None else I
+    if H % QUANT_GROUP or I % QUANT_GROUP:
+        raise ValueError("H and I must be multiples of 64")
+    base = seed_for(shape, M, layer) + 7919 * bits if seed is None else seed
+    seqs = np.random.SeedSequence(base).spawn(2 + 2 * E + 1)
+    rstd = shape.router_std if shape.router_std is not None else 1.0 / math.sqrt(H)
+    x = np.empty((M, H), dtype=np.uint16)
+    w_router = np.empty((E, H), dtype=np.uint16)
+    _normal_bf16_into(x, seqs[0], 1.0)
+    _normal_bf16_into(w_router, seqs[1], rstd)
+    w13 = [_quantized_matrix(2 * I, H, bits, seqs[2 + e]) for e in range(E)]
+    w2 = [_quantized_matrix(H, I, bits, seqs[2 + E + e]) for e in range(E)]
+    bias = None
+    if shape.zipf_s is not None:
+        rank = np.random.Generator(np.random.PCG64(seqs[-1])).permutation(E) + 1
+        bias = (-shape.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
+    return dict(x=x, w_router=w_router, logit_bias=bias,
+                w13_q=np.stack([m[0] for m in w13]), w13_scales=np.stack([m[1] for m in w13]),
+                w13_biases=np.stack([m[2] for m in w13]),
+                w2_q=np.stack([m[0] for m in w2]), w2_scales=np.stack([m[1] for m in w2]),
+                w2_biases=np.stack([m[2] for m in w2]),
+                M=M, E=E, top_k=top_k, H=H, I=I, bits=bits,
+                renormalize=shape.renormalize, name=shape.name)

@@ -24,4 +24,8 @@ from .moe_oracle import (  # noqa: F401
     layer_forward,
     combine_from_act,
     forward,
+    unpack_codes,
+    dequantize_affine,
+    forward_quantized,
+    QUANT_GROUP,
 )

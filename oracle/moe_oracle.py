@@ -149,12 +149,20 @@ def swiglu(h: np.ndarray, I: int) -> np.ndarray:
     return silu * u
 
 
+def _weights(w: np.ndarray) -> np.ndarray:
+    """An expert's weight matrix as float64: bf16 bit patterns are widened,
+    real-valued matrices (dequantized weights) are taken as they are."""
+    w = np.asarray(w)
+    return widen_bf16(w) if w.dtype == np.uint16 else w.astype(np.float64)
+
+
 def expert_ffn(x_rows: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray,
                return_act: bool = False):
     """f_e on a stack of rows: h = x W13_e^T ([n, 2I]), a = SwiGLU(h),
-    y = a W2_e^T ([n, H]).  x_rows float64 [n, H]; weights bf16 bits."""
-    W13 = widen_bf16(w13_e)
-    W2 = widen_bf16(w2_e)
+    y = a W2_e^T ([n, H]).  x_rows float64 [n, H]; weights bf16 bits (or
+    real-valued matrices)."""
+    W13 = _weights(w13_e)
+    W2 = _weights(w2_e)
     I = W2.shape[1]
     h = x_rows @ W13.T
     a = swiglu(h, I)
@@ -258,3 +266,76 @@ def forward(layer: dict, block_m: int | None = None,
         out["align"] = align(ids, layer["E"], block_m)
     out["y"] = layer_forward(x, layer["w13"], layer["w2"], ids, wts, tokens)
     return out
+
+
+# ---------------------------------------------------------------------------
+# group-quantized expert weights.  The MLX page's kernels read weights in the
+# affine group format (kernel names affine_qmv ... gs_64_b_4: group size 64,
+# 4 bits; 6 and 8 bits are discussed too) and the page's open question is a
+# kernel that tolerates a K that is not a multiple of its block (K = 1408).
+# Readings (the page names the format, not its layout): each row of a weight
+# matrix holds K codes q in [0, 2^bits); codes are packed little-end first
+# into 32-bit words (element i of a row is bits [bits*i, bits*(i+1)) of the
+# row's bit stream); each group of 64 consecutive elements of a row has one
+# scale s and one bias b (bf16), and the weight is w = s * q + b.
+# ---------------------------------------------------------------------------
+
+QUANT_GROUP = 64
+
+
+def unpack_codes(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Codes of a packed weight array [..., K * bits / 32] uint32 ->
+    [..., K] integers (element i: bits [bits*(i % per), ...) of word
+    i // per, least significant first; per = 32 / bits)."""
+    per = 32 // bits
+    w = np.asarray(words, dtype=np.uint32)
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
+    q = (w[..., :, None] >> shifts) & np.uint32((1 << bits) - 1)
+    return q.reshape(*w.shape[:-1], w.shape[-1] * per)[..., :K].astype(np.int64)
+
+
+def dequantize_affine(words: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                      bits: int, K: int, group: int = QUANT_GROUP) -> np.ndarray:
+    """w[..., i] = s[..., i // group] * q[..., i] + b[..., i // group], in
+    float64 (scales and biases are bf16 bit patterns, widened exactly)."""
+    q = unpack_codes(words, bits, K).astype(np.float64)
+    S = np.repeat(widen_bf16(scales), group, axis=-1)[..., :K]
+    B = np.repeat(widen_bf16(biases), group, axis=-1)[..., :K]
+    return S * q + B
+
+
+class DequantizedExperts:
+    """Expert e's weight matrix on demand, dequantized (float64)."""
+
+    def __init__(self, words, scales, biases, bits: int, K: int):
+        self.words, self.scales, self.biases = words, scales, biases
+        self.bits, self.K = bits, K
+
+    def __getitem__(self, e: int) -> np.ndarray:
+        return dequantize_affine(self.words[e], self.scales[e], self.biases[e], self.bits,
+                                 self.K)
+
+    @property
+    def shape(self):
+        return (self.words.shape[0], self.words.shape[1], self.K)
+
+
+def forward_quantized(layer: dict, tokens: np.ndarray | None = None) -> dict:
+    """The layer with group-quantized expert weights (a dict made by
+    ``moe_workloads.make_quantized_layer``): routing exactly as ``forward``
+    (the router stays bf16), then the same grouped expert FFNs and weighted
+    sum on the dequantized W13 and W2."""
+    x = layer["x"]
+    M, H = x.shape
+    I = layer["I"]
+    bits = layer["bits"]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    r = route(x[tokens], layer["w_router"], layer["top_k"], layer["renormalize"],
+              layer.get("logit_bias"))
+    ids = np.zeros((M, layer["top_k"]), dtype=np.int32)
+    wts = np.zeros((M, layer["top_k"]))
+    ids[tokens] = r["topk_ids"]
+    wts[tokens] = r["topk_weights"]
+    w13 = DequantizedExperts(layer["w13_q"], layer["w13_scales"], layer["w13_biases"], bits, H)
+    w2 = DequantizedExperts(layer["w2_q"], layer["w2_scales"], layer["w2_biases"], bits, I)
+    return dict(route=r, tokens=tokens, y=layer_forward(x, w13, w2, ids, wts, tokens))
