@@ -269,11 +269,12 @@ def forward(layer: dict, block_m: int | None = None,
 
 
 # ---------------------------------------------------------------------------
-# group-quantized expert weights.  The MLX page's kernels read weights in the
-# affine group format (kernel names affine_qmv ... gs_64_b_4: group size 64,
-# 4 bits; 6 and 8 bits are discussed too) and the page's open question is a
-# kernel that tolerates a K that is not a multiple of its block (K = 1408).
-# Readings (the page names the format, not its layout): each row of a weight
+# group-quantized expert weights.  In the MLX part of the page "SGLang issue
+# #22283" (GitHub thread) the kernels read weights in the affine group format
+# (kernel names affine_qmv ... gs_64_b_4: group size 64, 4 bits; 6 and 8
+# bits are discussed too) and the thread's open question is a kernel that
+# tolerates a K that is not a multiple of its block (K = 1408).
+# Readings (the thread names the format, not its layout): each row of a weight
 # matrix holds K codes q in [0, 2^bits); codes are packed little-end first
 # into 32-bit words (element i of a row is bits [bits*i, bits*(i+1)) of the
 # row's bit stream); each group of 64 consecutive elements of a row has one

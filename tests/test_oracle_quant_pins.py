@@ -1,6 +1,7 @@
 """Pins of the oracle's group-quantized weights (CPU only).
 
-The oracle reads the affine group format the MLX page names (64-element
+The oracle reads the affine group format that the MLX part of the page
+"SGLang issue #22283" names (64-element
 groups, 4 or 8 bits; w = s * q + b per group, codes packed least significant
 first into 32-bit words).  Each function is pinned to something other than
 itself:
