@@ -66,6 +66,8 @@ typedef enum moe_status {
 #define MOE_VARIANT_STREAM 1  /* weight-streaming MFMA kernel (about one row per expert) */
 #define MOE_VARIANT_PAIR_GEMV 2  /* per-pair GEMVs (block_m 1; moe_forward uses them,
                                     with no index lists, when M*top_k*4 <= E) */
+#define MOE_VARIANT_PAIR_GEMV_QUANT 3  /* moe_forward_quantized: per-pair GEMVs on
+                                          group-quantized weights */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -218,6 +220,51 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
                 int M, int E, int top_k, int H, int I, int renormalize,
                 uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
                 void* workspace, size_t ws_bytes, moe_dispatch_info* info, void* stream);
+
+/*
+ * Group-quantized expert weights (host struct of device pointers): the
+ * affine group format in the MLX part of the page "SGLang issue #22283"
+ * (GitHub thread): its kernels read 64-element-group, 4-bit weights
+ * (affine_qmv ... gs_64_b_4); 6 and 8 bits are discussed too.  Each row of
+ * W13 [E, 2I, H] and W2 [E, H, I] holds K codes q in [0, 2^bits), packed
+ * least significant first into 32-bit words (element i of a row is bits
+ * [bits*i, bits*(i+1)) of the row's bit stream); each group of 64
+ * consecutive elements of a row has one bf16 scale s and one bf16 bias b,
+ * and the weight is w = s*q + b.
+ */
+typedef struct moe_quantized_weights {
+  int bits;                      /* 4 or 8                                   */
+  int group_size;                /* 64                                       */
+  const uint32_t* w13_q;         /* [E, 2I, H*bits/32] packed codes          */
+  const uint16_t* w13_scales;    /* [E, 2I, H/64] bf16                       */
+  const uint16_t* w13_biases;    /* [E, 2I, H/64] bf16                       */
+  const uint32_t* w2_q;          /* [E, H, I*bits/32]                        */
+  const uint16_t* w2_scales;     /* [E, H, I/64] bf16                        */
+  const uint16_t* w2_biases;     /* [E, H, I/64] bf16                        */
+} moe_quantized_weights;
+
+/*
+ * moe_forward_quantized -- the layer of moe_forward with group-quantized
+ * expert weights (the router stays bf16).  Every pair runs as its own GEMV
+ * against its expert's dequantized rows (page "Mixture of Experts in vLLM
+ * ...", sub-section "Small batches skip the sort"; no index lists), the
+ * group's scale and bias applied per 16-byte unit of codes; GEMV 2 adds the
+ * weighted top_k rows per token in one launch.  Each pair reads its
+ * expert's whole weights, so this suits small batches (it is correct for
+ * any M).  Four launches: router logits, top-k, GEMV 1, GEMV 2.
+ *
+ *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, workspace:
+ *                as for moe_forward (same workspace size)
+ *   qw           host struct of device pointers, all 16-byte aligned
+ * H and I must be multiples of 64 (MOE_ERR_UNSUPPORTED otherwise); a K that
+ * is not a multiple of the kernels' 256- or 512-element passes is fine.
+ * info->variant reads MOE_VARIANT_PAIR_GEMV_QUANT.
+ */
+int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                          const moe_quantized_weights* qw, int M, int E, int top_k, int H, int I,
+                          int renormalize, uint16_t* out, int32_t* topk_ids_out,
+                          float* topk_weights_out, void* workspace, size_t ws_bytes,
+                          moe_dispatch_info* info, void* stream);
 
 #ifdef __cplusplus
 }

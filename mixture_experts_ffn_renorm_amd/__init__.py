@@ -7,8 +7,9 @@ and there is no CPU fallback -- if the library is missing, importing the
 binding works but every call raises.
 
 Function names match the C ABI: moe_route, moe_align,
-moe_grouped_gemm_w13_act, moe_grouped_gemm_w2_combine, moe_forward, plus
-moe_workspace_size, moe_pick_block_m and moe_strerror.
+moe_grouped_gemm_w13_act, moe_grouped_gemm_w2_combine, moe_forward,
+moe_forward_quantized, plus moe_workspace_size, moe_pick_block_m and
+moe_strerror.
 """
 
 from __future__ import annotations
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
 MOE_VARIANT_TILED = 0
 MOE_VARIANT_STREAM = 1
 MOE_VARIANT_PAIR_GEMV = 2
+MOE_VARIANT_PAIR_GEMV_QUANT = 3
 
 _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -44,6 +46,13 @@ class DispatchInfo(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class QuantizedWeights(ctypes.Structure):
+    """moe_quantized_weights: bits, group size and six device pointers."""
+    _fields_ = [("bits", _c_int), ("group_size", _c_int),
+                ("w13_q", _c_void_p), ("w13_scales", _c_void_p), ("w13_biases", _c_void_p),
+                ("w2_q", _c_void_p), ("w2_scales", _c_void_p), ("w2_biases", _c_void_p)]
+
+
 _SIGNATURES = {
     "moe_workspace_size": (_c_size_t, [_c_int] * 5),
     "moe_strerror": (ctypes.c_char_p, [_c_int]),
@@ -62,6 +71,10 @@ _SIGNATURES = {
     "moe_forward": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
                     [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                      ctypes.POINTER(DispatchInfo), _c_void_p]),
+    "moe_forward_quantized": (_c_int, [_c_void_p] * 3 + [ctypes.POINTER(QuantizedWeights)] +
+                              [_c_int] * 6 +
+                              [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                               ctypes.POINTER(DispatchInfo), _c_void_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -303,4 +316,52 @@ def moe_forward(x, w_router, w13, w2, top_k: int, renormalize: bool = True,
         int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
         _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
     _raise("moe_forward", st)
+    return out, info.as_dict()
+
+
+def moe_forward_quantized(x, w_router, qweights: dict, top_k: int, renormalize: bool = True,
+                          logit_bias=None, out=None, topk_ids_out=None, topk_weights_out=None,
+                          ws=None, stream=None):
+    """The layer with group-quantized expert weights.  ``qweights`` holds
+    ``bits`` (4 or 8), ``w13_q`` [E, 2I, H*bits/32] and ``w2_q``
+    [E, H, I*bits/32] (int32 or uint32 words of packed codes), and
+    ``w13_scales``, ``w13_biases`` [E, 2I, H/64], ``w2_scales``,
+    ``w2_biases`` [E, H, I/64] (bf16).  Returns (out [M, H] bf16, dispatch
+    info dict)."""
+    torch = _torch()
+    M, H = x.shape
+    E = w_router.shape[0]
+    bits = int(qweights["bits"])
+    I = qweights["w2_q"].shape[2] * 32 // bits if bits in (4, 8) else 0
+    words = (torch.int32, getattr(torch, "uint32", torch.int32))
+    _check(x, "x", _bf16_types())
+    _check(w_router, "w_router", _bf16_types(), (E, H))
+    if bits in (4, 8):
+        for name, shape, types in (("w13_q", (E, 2 * I, H * bits // 32), words),
+                                   ("w13_scales", (E, 2 * I, H // 64), _bf16_types()),
+                                   ("w13_biases", (E, 2 * I, H // 64), _bf16_types()),
+                                   ("w2_q", (E, H, I * bits // 32), words),
+                                   ("w2_scales", (E, H, I // 64), _bf16_types()),
+                                   ("w2_biases", (E, H, I // 64), _bf16_types())):
+            _check(qweights[name], name, types, shape)
+    if logit_bias is not None:
+        _check(logit_bias, "logit_bias", (torch.float32,), (E,))
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", _bf16_types(), (M, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", (torch.int32,), (M, top_k))
+    if topk_weights_out is not None:
+        _check(topk_weights_out, "topk_weights_out", (torch.float32,), (M, top_k))
+    if ws is None:
+        ws = workspace(M, E, top_k, H, max(I, 1), x.device)
+    qw = QuantizedWeights(bits, int(qweights.get("group_size", 64)),
+                          *(_ptr(qweights.get(n)) for n in ("w13_q", "w13_scales", "w13_biases",
+                                                            "w2_q", "w2_scales", "w2_biases")))
+    info = DispatchInfo()
+    st = library().moe_forward_quantized(
+        _ptr(x), _ptr(w_router), _ptr(logit_bias), ctypes.byref(qw), M, E, top_k, H, I,
+        int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
+        _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
+    _raise("moe_forward_quantized", st)
     return out, info.as_dict()

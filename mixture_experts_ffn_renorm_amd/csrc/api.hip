@@ -386,4 +386,43 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
   return run_gemm2(g, s);
 }
 
+int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                          const moe_quantized_weights* qw, int M, int E, int top_k, int H, int I,
+                          int renormalize, uint16_t* out, int32_t* topk_ids_out,
+                          float* topk_weights_out, void* workspace, size_t ws_bytes,
+                          moe_dispatch_info* info, void* stream) {
+  int st = check_sizes(M, E, top_k, H, I);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (qw == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((qw->bits != 4 && qw->bits != 8) || qw->group_size != 64) return MOE_ERR_UNSUPPORTED;
+  if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  fill_info(info, 1, H, I, M == 0 ? 0 : kPairGemvForwardLaunches, 0);
+  if (info != nullptr) info->variant = MOE_VARIANT_PAIR_GEMV_QUANT;
+  if (M == 0) return MOE_OK;
+  if (!x || !w_router || !out || !qw->w13_q || !qw->w13_scales || !qw->w13_biases ||
+      !qw->w2_q || !qw->w2_scales || !qw->w2_biases)
+    return MOE_ERR_INVALID_ARG;
+  if (!a16(x) || !a16(w_router) || !a16(out) || !a16(workspace) || !a16(qw->w13_q) ||
+      !a16(qw->w2_q) || !a16(qw->w13_scales) || !a16(qw->w13_biases) || !a16(qw->w2_scales) ||
+      !a16(qw->w2_biases))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = forward_layout(M, E, top_k, H, I, 1);
+  if (workspace == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(ws + L.wts);
+  RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
+               reinterpret_cast<float*>(ws + L.logits), ids, wts, nullptr, 0};
+  QPairGemvArgs q{x, qw->w13_q, qw->w13_scales, qw->w13_biases, qw->w2_q, qw->w2_scales,
+                  qw->w2_biases, ids, wts, M, top_k, H, I, qw->bits,
+                  reinterpret_cast<uint16_t*>(ws + L.act), out};
+  MOE_TRY_HIP(launch_route_logits(ra, s));
+  MOE_TRY_HIP(launch_route_topk(ra, s));
+  MOE_TRY_HIP(launch_qpair_gemv1(q, s));
+  MOE_TRY_HIP(launch_qpair_gemv2(q, s));
+  return MOE_OK;
+}
+
 }  // extern "C"

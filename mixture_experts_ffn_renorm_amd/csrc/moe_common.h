@@ -371,6 +371,26 @@ struct PairGemvArgs {
   const int32_t* expert_ids;  // block_m 1 lists: expert of block b
   float* partial;             // [M*top_k, H] fp32 (lists form of GEMV 2)
 };
+// Per-pair GEMVs on group-quantized expert weights (affine, 64-element
+// groups, 4 or 8 bits): GEMV 1 writes act [P, I]; GEMV 2 multiplies,
+// weights and sums each token's top_k rows into out [M, H].
+struct QPairGemvArgs {
+  const uint16_t* x;            // [M, H]
+  const uint32_t* w13q;         // [E, 2I, H*bits/32] packed codes
+  const uint16_t* w13_scales;   // [E, 2I, H/64] bf16
+  const uint16_t* w13_biases;   // [E, 2I, H/64] bf16
+  const uint32_t* w2q;          // [E, H, I*bits/32]
+  const uint16_t* w2_scales;    // [E, H, I/64]
+  const uint16_t* w2_biases;    // [E, H, I/64]
+  const int32_t* topk_ids;      // [M, top_k]
+  const float* topk_weights;    // [M, top_k]
+  int M, top_k, H, I, bits;
+  uint16_t* act;                // [M*top_k, I]
+  uint16_t* out;                // [M, H]
+};
+hipError_t launch_qpair_gemv1(const QPairGemvArgs& a, hipStream_t s);
+hipError_t launch_qpair_gemv2(const QPairGemvArgs& a, hipStream_t s);
+
 hipError_t launch_pair_gemv1(const PairGemvArgs& a, hipStream_t s);
 hipError_t launch_pair_gemv2(const PairGemvArgs& a, hipStream_t s);
 

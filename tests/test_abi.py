@@ -150,3 +150,34 @@ def test_dispatch_info_forward_readout():
     assert lib.moe_forward(NULL, NULL, NULL, NULL, NULL, 0, 60, 4, 2048, 1408, 1, NULL, NULL,
                            NULL, NULL, 0, ctypes.byref(info), NULL) == 0
     assert info.variant == moe.MOE_VARIANT_STREAM and info.k_tail == 1
+
+
+@pytest.mark.parametrize("bits,group,H,I,M,status", [
+    (5, 64, 2048, 768, 4, -2),        # bits must be 4 or 8
+    (4, 32, 2048, 768, 4, -2),        # groups of 64 only
+    (4, 64, 2048 + 8, 768, 4, -2),    # H % 64
+    (8, 64, 2048, 768 + 8, 4, -2),    # I % 64
+    (4, 64, 2048, 768, 4, -1),        # null pointers
+    (8, 64, 2048, 768, 0, 0),         # M = 0: no launch
+])
+def test_forward_quantized_argument_checks(bits, group, H, I, M, status):
+    moe = _moe()
+    lib = moe.library()
+    qw = moe.QuantizedWeights(bits, group)
+    info = moe.DispatchInfo()
+    st = lib.moe_forward_quantized(NULL, NULL, NULL, ctypes.byref(qw), M, 128, 8, H, I, 1,
+                                   NULL, NULL, NULL, NULL, 0, ctypes.byref(info), NULL)
+    assert st == status
+    if status == 0:
+        assert info.variant == moe.MOE_VARIANT_PAIR_GEMV_QUANT and info.launches == 0
+
+
+def test_forward_quantized_null_struct_and_workspace():
+    moe = _moe()
+    lib = moe.library()
+    assert lib.moe_forward_quantized(NULL, NULL, NULL, NULL, 4, 128, 8, 2048, 768, 1, NULL, NULL,
+                                     NULL, NULL, 0, NULL, NULL) == -1
+    fake = ctypes.c_void_p(0x10000)      # never dereferenced: the size check fails first
+    qw = moe.QuantizedWeights(4, 64, *([0x10000] * 6))
+    assert lib.moe_forward_quantized(fake, fake, NULL, ctypes.byref(qw), 4, 128, 8, 2048, 768, 1,
+                                     fake, NULL, NULL, fake, 1024, NULL, NULL) == -3
