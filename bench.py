@@ -14,6 +14,9 @@ Prints ONE JSON line:
                    runs on), against the MI355X peak
   cpu_baseline     the CPU oracle on a bounded sample of the same workload
   kernels          mean duration of every kernel of the step (events)
+  quantized        context: moe_forward_quantized (affine 64-element groups,
+                   4 and 8 bits) on the same shape at M = 1 and 4, one captured
+                   HIP graph of the L layers replayed
 Default workload: the Qwen3-30B-A3B-shaped decode layer (E=128, top_k=8,
 H=2048, I=768) at M=64 tokens.
 """
@@ -38,7 +41,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 DEFAULT_WORKLOAD = ("qwen3_decode", 64)
 
 
-VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv"}
+VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant"}
 
 
 def parse_args():
@@ -53,6 +56,10 @@ def parse_args():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the many-layer stack (eager and HIP-graph replay) figures")
+    ap.add_argument("--no-quant", action="store_true",
+                    help="skip the group-quantized (4- and 8-bit) small-batch figures")
+    ap.add_argument("--quant-sizes", default="4:1,4:4,8:1,8:4",
+                    help="bits:M pairs of the quantized figures (default 4:1,4:4,8:1,8:4)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration runs)")
     return ap.parse_args()
@@ -339,11 +346,86 @@ def main():
                            "layer_tokens_per_s_graph": round(M * L / graph_s, 1)}
         del graph, stack
 
+    # ---- group-quantized expert weights at small batches (context) ----
+    if not args.no_quant and shape.H % 64 == 0 and shape.I % 64 == 0 and M <= 64:
+        sizes = [tuple(int(v) for v in p.split(":")) for p in args.quant_sizes.split(",") if p]
+        result["quantized"] = quantized_figures(shape, L, x, dev, max(10, min(args.steps, 50)),
+                                                sizes)
+
     # ---- the oracle on the host, on a bounded sample ----
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, M, layers[0], x)
 
     print(json.dumps(result), flush=True)
+
+
+def quantized_alg_bytes(shape, M, bits, touched):
+    """Per-forward algorithmic bytes with group-quantized expert weights:
+    per touched expert the 3*H*I codes (bits/8 bytes each) and 4 bytes of
+    bf16 scale and bias per 64-element group; plus the bf16 router and x in
+    and out."""
+    E, H, I = shape.E, shape.H, shape.I
+    per_expert = 3 * H * I * bits // 8 + (3 * H * I // 64) * 4
+    return touched * per_expert + 2 * E * H + 4 * M * H
+
+
+def quantized_figures(shape, L, x, dev, reps, sizes):
+    """moe_forward_quantized at the (bits, M) pairs of `sizes` over L
+    device-drawn quantized layers: the L calls captured once into a HIP
+    graph, replayed `reps` times (host marshalling out of the timed
+    region)."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as wl
+    import mixture_experts_ffn_renorm_amd as moe
+
+    E, k, H, I = shape.E, shape.top_k, shape.H, shape.I
+    res = {}
+    ws = moe.workspace(max(m for _, m in sizes), E, k, H, I, dev)
+    for bits in sorted({b for b, _ in sizes}):
+        qlayers = [wl.make_device_quantized_layer(shape, 4, bits, layer=i + 1, device=dev)
+                   for i in range(L)]
+        for Ms in sorted(m for b, m in sizes if b == bits):
+            xs = x[:Ms].contiguous() if x.shape[0] >= Ms else \
+                torch.randn((Ms, H), device=dev).to(torch.bfloat16)
+            out = torch.empty((Ms, H), dtype=torch.bfloat16, device=dev)
+            ids = [torch.empty((Ms, k), dtype=torch.int32, device=dev) for _ in range(L)]
+
+            def run_all():
+                for i, ql in enumerate(qlayers):
+                    _, info = moe.moe_forward_quantized(
+                        xs, ql["w_router"], ql["q"], k, shape.renormalize,
+                        logit_bias=ql["logit_bias"], out=out, topk_ids_out=ids[i], ws=ws)
+                return info
+
+            info = run_all()
+            torch.cuda.synchronize()
+            touched = float(np.mean([torch.unique(t).numel() for t in ids]))
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                run_all()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / (reps * L)
+            alg = quantized_alg_bytes(shape, Ms, bits, touched)
+            res[f"b{bits}_M{Ms}"] = {
+                "bits": bits, "M": Ms, "us_per_layer": round(us, 2),
+                "tokens_per_s": round(Ms / (us * 1e-6), 1),
+                "alg_bytes": int(alg), "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mean_touched_experts": touched, "variant": VARIANT_NAMES[info["variant"]],
+                "launches": info["launches"]}
+            del graph
+        del qlayers
+    return res
 
 
 def cpu_baseline(shape, M, lay, x):

@@ -62,6 +62,52 @@ __device__ __forceinline__ float sum_unit(const u32x4* xv) {
   return s;
 }
 
+// 4-bit units on the bf16 dot-2 instruction: a code q in [0, 16) becomes the
+// bf16 value 128 + q exactly (exponent of 128, q in the low mantissa bits),
+// so a unit's codes turn into bf16 pairs with one shift and one and-or per
+// pair, and sum (128 + q_i) x_i - 128 * sum x_i = sum q_i x_i.  Code word w
+// holds elements 8w .. 8w + 7; its pair i (i < 4) takes elements i and
+// i + 4 (bits 4i and 16 + 4i), and x is regrouped once per unit to match.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+struct XPairs4 {
+  uint32_t y[16];   // (x_i, x_{i+4}) of each 8-element word, as bf16 pairs
+  float sx;         // sum of the unit's 32 x
+};
+
+__device__ __forceinline__ XPairs4 regroup_x4(const u32x4* xv) {
+  XPairs4 r;
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const u32x4 X = xv[w];   // (x0,x1) (x2,x3) (x4,x5) (x6,x7) of word w
+    r.y[4 * w + 0] = __builtin_amdgcn_perm(X[2], X[0], 0x05040100u);   // (x0, x4)
+    r.y[4 * w + 1] = __builtin_amdgcn_perm(X[2], X[0], 0x07060302u);   // (x1, x5)
+    r.y[4 * w + 2] = __builtin_amdgcn_perm(X[3], X[1], 0x05040100u);   // (x2, x6)
+    r.y[4 * w + 3] = __builtin_amdgcn_perm(X[3], X[1], 0x07060302u);   // (x3, x7)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = dot2_bf16(X[j], 0x3f803f80u, s);   // (1, 1)
+  }
+  r.sx = s;
+  return r;
+}
+
+// sum q_i x_i over one 4-bit unit
+__device__ __forceinline__ float dot_unit4(const u32x4 codes, const XPairs4& xp) {
+  float d = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d = dot2_bf16(((codes[w] >> (4 * i)) & 0x000f000fu) | 0x43004300u, xp.y[4 * w + i], d);
+  return d - 128.f * xp.sx;
+}
+
 __device__ __forceinline__ float bf16_load(const uint16_t* p) {
   return __uint_as_float((uint32_t)*p << 16);
 }
@@ -118,9 +164,16 @@ __global__ __launch_bounds__(64 * kQ1Waves) void qgemv_w13_kernel(
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const bool ok = base + 64 * c < nunit;
-      const float sx = sum_unit<BITS>(xv[c]);
-      const float dg = gs[c] * dot_unit<BITS>(cg[c], xv[c]) + gb[c] * sx;
-      const float du = us[c] * dot_unit<BITS>(cu[c], xv[c]) + ub[c] * sx;
+      float dg, du;
+      if constexpr (BITS == 4) {
+        const XPairs4 xp = regroup_x4(xv[c]);
+        dg = gs[c] * dot_unit4(cg[c], xp) + gb[c] * xp.sx;
+        du = us[c] * dot_unit4(cu[c], xp) + ub[c] * xp.sx;
+      } else {
+        const float sx = sum_unit<BITS>(xv[c]);
+        dg = gs[c] * dot_unit<BITS>(cg[c], xv[c]) + gb[c] * sx;
+        du = us[c] * dot_unit<BITS>(cu[c], xv[c]) + ub[c] * sx;
+      }
       ag += ok ? dg : 0.f;
       au += ok ? du : 0.f;
     }
@@ -130,7 +183,9 @@ __global__ __launch_bounds__(64 * kQ1Waves) void qgemv_w13_kernel(
   if (lane == 0) act[(size_t)p * I + f] = (uint16_t)f32_to_bf16(silu_mul(ag, au));
 }
 
-template <int BITS, int NC>
+// SPLIT = 2 (rows of at most 32 units): the two half-waves take two of the
+// four columns each, so that short rows keep most lanes busy.
+template <int BITS, int NC, int SPLIT>
 __global__ __launch_bounds__(64 * kQMaxWaves) void qgemv_w2_sum_kernel(
     const uint16_t* __restrict__ act, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
@@ -138,37 +193,40 @@ __global__ __launch_bounds__(64 * kQMaxWaves) void qgemv_w2_sum_kernel(
     int H, int I, uint16_t* __restrict__ out) {
   constexpr int kEU = 128 / BITS;
   constexpr int kXU = kEU / 8;
+  constexpr int kLanes = 64 / SPLIT;        // lanes per column group
+  constexpr int kRows = kQ2Cols / SPLIT;    // columns per lane
   __shared__ float red[kQMaxWaves][kQ2Cols];
   const int t = blockIdx.y;
   const int h0 = blockIdx.x * kQ2Cols;   // H % 64 == 0: all columns exist
   const int lane = threadIdx.x & 63;
+  const int half = lane / kLanes, ll = lane % kLanes;
   // wave-uniform: the slot's expert id and weight come in through scalar loads
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;    // <= top_k
   const int nunit = I / kEU, ng = I / kGroup;
-  float acc[kQ2Cols];
+  float acc[kRows];
 #pragma unroll
-  for (int r = 0; r < kQ2Cols; ++r) acc[r] = 0.f;
+  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
   for (int j = w; j < top_k; j += nwaves) {
     const int p = t * top_k + j;
     const int e = topk_ids[p];
-    const size_t row0 = (size_t)e * H + h0;
+    const size_t row0 = (size_t)e * H + h0 + half * kRows;
     const float wt = topk_weights[p];
     const u32x4* ar = reinterpret_cast<const u32x4*>(act + (size_t)p * I);
-    float s[kQ2Cols];
+    float s[kRows];
 #pragma unroll
-    for (int r = 0; r < kQ2Cols; ++r) s[r] = 0.f;
-    for (int base = lane; base < nunit + lane; base += 64 * NC) {
-      u32x4 cw[kQ2Cols][NC], av[NC][kXU];
-      float ws[kQ2Cols][NC], wb[kQ2Cols][NC];
+    for (int r = 0; r < kRows; ++r) s[r] = 0.f;
+    for (int base = ll; base < nunit + ll; base += kLanes * NC) {
+      u32x4 cw[kRows][NC], av[NC][kXU];
+      float ws[kRows][NC], wb[kRows][NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int u = base + 64 * c;
+        const int u = base + kLanes * c;
         const int g = (u < nunit ? u : 0) * kEU / kGroup;
 #pragma unroll
-        for (int r = 0; r < kQ2Cols; ++r) {
+        for (int r = 0; r < kRows; ++r) {
           cw[r][c] = load_unit<true>(reinterpret_cast<const u32x4*>(wq) + (row0 + r) * nunit, u,
-                                        nunit);
+                                     nunit);
           ws[r][c] = bf16_load(sc + (row0 + r) * ng + g);
           wb[r][c] = bf16_load(bi + (row0 + r) * ng + g);
         }
@@ -178,22 +236,34 @@ __global__ __launch_bounds__(64 * kQMaxWaves) void qgemv_w2_sum_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bool ok = base + 64 * c < nunit;
-        const float sx = sum_unit<BITS>(av[c]);
+        const bool ok = base + kLanes * c < nunit;
+        if constexpr (BITS == 4) {
+          const XPairs4 xp = regroup_x4(av[c]);
 #pragma unroll
-        for (int r = 0; r < kQ2Cols; ++r) {
-          const float d = ws[r][c] * dot_unit<BITS>(cw[r][c], av[c]) + wb[r][c] * sx;
-          s[r] += ok ? d : 0.f;
+          for (int r = 0; r < kRows; ++r) {
+            const float d = ws[r][c] * dot_unit4(cw[r][c], xp) + wb[r][c] * xp.sx;
+            s[r] += ok ? d : 0.f;
+          }
+        } else {
+          const float sx = sum_unit<BITS>(av[c]);
+#pragma unroll
+          for (int r = 0; r < kRows; ++r) {
+            const float d = ws[r][c] * dot_unit<BITS>(cw[r][c], av[c]) + wb[r][c] * sx;
+            s[r] += ok ? d : 0.f;
+          }
         }
       }
     }
 #pragma unroll
-    for (int r = 0; r < kQ2Cols; ++r) acc[r] = __builtin_fmaf(wt, s[r], acc[r]);
+    for (int r = 0; r < kRows; ++r) acc[r] = __builtin_fmaf(wt, s[r], acc[r]);
   }
+  // sum over the lanes of each column group (xor offsets stay inside it)
 #pragma unroll
-  for (int r = 0; r < kQ2Cols; ++r) {
-    const float v = wave_sum(acc[r]);
-    if (lane == 0) red[w][r] = v;
+  for (int r = 0; r < kRows; ++r) {
+    float v = acc[r];
+#pragma unroll
+    for (int d = kLanes / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    if (ll == 0) red[w][half * kRows + r] = v;
   }
   __syncthreads();
   if (threadIdx.x < kQ2Cols) {
@@ -217,12 +287,12 @@ void launch_q1(const moe_host::QPairGemvArgs& a, hipStream_t s) {
                      a.w13_scales, a.w13_biases, a.topk_ids, a.top_k, a.H, a.I, a.act);
 }
 
-template <int BITS, int NC>
+template <int BITS, int NC, int SPLIT = 1>
 void launch_q2(const moe_host::QPairGemvArgs& a, hipStream_t s) {
   const int waves = a.top_k < kQMaxWaves ? a.top_k : kQMaxWaves;
-  hipLaunchKernelGGL((qgemv_w2_sum_kernel<BITS, NC>), dim3(a.H / kQ2Cols, a.M), dim3(64 * waves),
-                     0, s, a.act, a.w2q, a.w2_scales, a.w2_biases, a.topk_ids, a.topk_weights,
-                     a.top_k, a.H, a.I, a.out);
+  hipLaunchKernelGGL((qgemv_w2_sum_kernel<BITS, NC, SPLIT>), dim3(a.H / kQ2Cols, a.M),
+                     dim3(64 * waves), 0, s, a.act, a.w2q, a.w2_scales, a.w2_biases, a.topk_ids,
+                     a.topk_weights, a.top_k, a.H, a.I, a.out);
 }
 
 template <int BITS>
@@ -241,7 +311,9 @@ void launch_q2_nc(const moe_host::QPairGemvArgs& a, hipStream_t s) {
   // (4 rows x 4 units would spill registers)
   constexpr int kMaxNC = BITS == 4 ? 2 : 4;
   const int n = units_per_lane(a.I * BITS / 128);
-  if (n == 1) {
+  if (a.I * BITS / 128 <= 32) {
+    launch_q2<BITS, 1, 2>(a, s);
+  } else if (n == 1) {
     launch_q2<BITS, 1>(a, s);
   } else if (n == 2 || kMaxNC == 2) {
     launch_q2<BITS, 2>(a, s);

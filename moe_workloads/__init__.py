@@ -299,3 +299,38 @@ def make_quantized_layer(shape: LayerShape | str, M: int, bits: int, layer: int 
                 w2_biases=np.stack([m[2] for m in w2]),
                 M=M, E=E, top_k=top_k, H=H, I=I, bits=bits,
                 renormalize=shape.renormalize, name=shape.name)
+
+
+def make_device_quantized_layer(shape: LayerShape | str, M: int, bits: int, layer: int,
+                                device) -> dict:
+    """Draw one extra timing layer with group-quantized expert weights
+    directly in device memory: uniformly random code words (int32), and per
+    64-element group scales and biases drawn as by :func:`make_quantized_layer`
+    (bf16), with torch's seeded generator on the device.  Returns a dict of
+    torch tensors w_router, logit_bias and the ``moe_forward_quantized``
+    weight dict under ``q``."""
+    import torch  # local import: the oracle side never needs torch
+
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    E, H, I = shape.E, shape.H, shape.I
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(shape, M, layer) + 7919 * bits)
+    rstd = shape.router_std if shape.router_std is not None else 1.0 / math.sqrt(H)
+    w_router = (torch.randn((E, H), generator=g, device=device) * rstd).to(torch.bfloat16)
+    q = {"bits": bits}
+    for name, rows, K in (("w13", 2 * I, H), ("w2", H, I)):
+        q[name + "_q"] = torch.randint(-2 ** 31, 2 ** 31 - 1, (E, rows, K * bits // 32),
+                                       generator=g, device=device, dtype=torch.int32)
+        a = math.sqrt(3.0 / K)
+        jit = torch.randn((2, E, rows, K // QUANT_GROUP), generator=g, device=device)
+        q[name + "_scales"] = ((2.0 * a / ((1 << bits) - 1)) * (1.0 + 0.1 * jit[0])).to(
+            torch.bfloat16)
+        q[name + "_biases"] = (-a * (1.0 + 0.1 * jit[1])).to(torch.bfloat16)
+    bias = None
+    if shape.zipf_s is not None:
+        rank = torch.randperm(E, generator=g, device=device).to(torch.float64) + 1
+        bias = (-shape.zipf_s * torch.log(rank)).to(torch.float32)
+    return dict(w_router=w_router, logit_bias=bias, q=q)
