@@ -41,17 +41,25 @@ constexpr int kG1Cols = 1;     // GEMV 1: act columns per wave (divides 8)
 constexpr int kMaxWaves = 8;   // GEMV 2: waves per workgroup, min(top_k, 8)
 constexpr int kG2Cols = 4;     // GEMV 2: output columns per workgroup (divides 8)
 
-// Sum over this lane's NC chunks of 8 bf16 products, in fp32.
+// Sum over this lane's NC chunks of 8 bf16 products, in fp32: the bf16
+// dot-2 instruction takes two adjacent elements of each operand as they sit
+// in memory (products exact in fp32, accumulated in fp32), so nothing is
+// unpacked.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// (the words come in by value: a bit cast of a vector-element lvalue would
+// read the vector's first element)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 template <int NC>
 __device__ __forceinline__ float dot_chunks(const u32x4 (&a)[NC], const u32x4 (&b)[NC], float s) {
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      s = __builtin_fmaf(__uint_as_float(a[c][q] << 16), __uint_as_float(b[c][q] << 16), s);
-      s = __builtin_fmaf(__uint_as_float(a[c][q] & 0xffff0000u),
-                         __uint_as_float(b[c][q] & 0xffff0000u), s);
-    }
+    for (int q = 0; q < 4; ++q) s = dot2_bf16(a[c][q], b[c][q], s);
   return s;
 }
 
@@ -120,7 +128,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_w2_sum_kernel(
   __shared__ float red[kMaxWaves][R];
   const int t = blockIdx.y;
   const int h0 = blockIdx.x * R;   // H % 8 == 0 and R divides 8: all R rows exist
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform: the slot's expert id and weight come in through scalar loads
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;   // <= top_k
   const int nchunk = I / 8;
   float acc[R];
@@ -128,6 +138,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_w2_sum_kernel(
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
   for (int j = w; j < top_k; j += nwaves) {
     const int p = t * top_k + j;
+    const float wt = topk_weights[p];
     const uint16_t* arow = act + (size_t)p * I;
     const uint16_t* wrow = w2 + ((size_t)topk_ids[p] * H + h0) * I;
     float s[R];
@@ -146,7 +157,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_w2_sum_kernel(
 #pragma unroll
       for (int r = 0; r < R; ++r) s[r] = dot_chunks<NC>(wv[r], av, s[r]);
     }
-    const float wt = topk_weights[p];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(wt, s[r], acc[r]);
   }
