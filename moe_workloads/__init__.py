@@ -334,3 +334,88 @@ def make_device_quantized_layer(shape: LayerShape | str, M: int, bits: int, laye
         rank = torch.randperm(E, generator=g, device=device).to(torch.float64) + 1
         bias = (-shape.zipf_s * torch.log(rank)).to(torch.float32)
     return dict(w_router=w_router, logit_bias=bias, q=q)
+
+
+MX_BLOCK = 32
+
+
+def _mx_matrix(rows: int, K: int, seq: np.random.SeedSequence):
+    """Random MXFP8 codes and scales of one expert matrix [rows, K]: E4M3
+    bytes with a random sign, exponent field uniform over 4..9 and mantissa
+    uniform over 0..7 (magnitudes 1/8 .. 3.75, no NaN codes), and per
+    32-element block an E8M0 scale code 127 - round(log2 sqrt K) - 1 + {-1,
+    0, 1}, so that the weights have a spread near 1/sqrt(K)."""
+    rng = np.random.Generator(np.random.PCG64(seq))
+    sign = rng.integers(0, 2, size=(rows, K), dtype=np.uint8) << 7
+    expo = rng.integers(4, 10, size=(rows, K), dtype=np.uint8) << 3
+    mant = rng.integers(0, 8, size=(rows, K), dtype=np.uint8)
+    base = 127 - int(round(math.log2(math.sqrt(K)))) - 1
+    scales = (base + rng.integers(-1, 2, size=(rows, K // MX_BLOCK))).astype(np.uint8)
+    return (sign | expo | mant).astype(np.uint8), scales
+
+
+def make_mx_layer(shape: LayerShape | str, M: int, layer: int = 0,
+                  E: Optional[int] = None, top_k: Optional[int] = None,
+                  H: Optional[int] = None, I: Optional[int] = None,
+                  seed: Optional[int] = None) -> dict:
+    """One synthetic layer with MXFP8 expert weights: x, w_router (bf16) and
+    the Zipf prior drawn as by :func:`make_layer`; W13 [E, 2I, H] and W2
+    [E, H, I] as E4M3 codes (``w13_codes``, uint8) and E8M0 scales per 32
+    elements (``w13_scales`` [E, 2I, H/32], uint8).  H and I must be
+    multiples of 32."""
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    E = shape.E if E is None else E
+    top_k = shape.top_k if top_k is None else top_k
+    H = shape.H if H is None else H
+    I = shape.I if I is None else I
+    if H % MX_BLOCK or I % MX_BLOCK:
+        raise ValueError("H and I must be multiples of 32")
+    base = seed_for(shape, M, layer) + 104729 if seed is None else seed
+    seqs = np.random.SeedSequence(base).spawn(2 + 2 * E + 1)
+    rstd = shape.router_std if shape.router_std is not None else 1.0 / math.sqrt(H)
+    x = np.empty((M, H), dtype=np.uint16)
+    w_router = np.empty((E, H), dtype=np.uint16)
+    _normal_bf16_into(x, seqs[0], 1.0)
+    _normal_bf16_into(w_router, seqs[1], rstd)
+    w13 = [_mx_matrix(2 * I, H, seqs[2 + e]) for e in range(E)]
+    w2 = [_mx_matrix(H, I, seqs[2 + E + e]) for e in range(E)]
+    bias = None
+    if shape.zipf_s is not None:
+        rank = np.random.Generator(np.random.PCG64(seqs[-1])).permutation(E) + 1
+        bias = (-shape.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
+    return dict(x=x, w_router=w_router, logit_bias=bias,
+                w13_codes=np.stack([m[0] for m in w13]), w13_scales=np.stack([m[1] for m in w13]),
+                w2_codes=np.stack([m[0] for m in w2]), w2_scales=np.stack([m[1] for m in w2]),
+                M=M, E=E, top_k=top_k, H=H, I=I, renormalize=shape.renormalize,
+                name=shape.name)
+
+
+def make_device_mx_layer(shape: LayerShape | str, M: int, layer: int, device) -> dict:
+    """An MXFP8 timing layer drawn directly in device memory with torch's
+    seeded generator (same recipe as :func:`make_mx_layer`).  Returns
+    w_router, logit_bias and the ``moe_forward_mxfp8`` weight dict under
+    ``w``."""
+    import torch  # local import: the oracle side never needs torch
+
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    E, H, I = shape.E, shape.H, shape.I
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(shape, M, layer) + 104729)
+    rstd = shape.router_std if shape.router_std is not None else 1.0 / math.sqrt(H)
+    w_router = (torch.randn((E, H), generator=g, device=device) * rstd).to(torch.bfloat16)
+    w = {}
+    for name, rows, K in (("w13", 2 * I, H), ("w2", H, I)):
+        sign = torch.randint(0, 2, (E, rows, K), generator=g, device=device, dtype=torch.uint8)
+        expo = torch.randint(4, 10, (E, rows, K), generator=g, device=device, dtype=torch.uint8)
+        mant = torch.randint(0, 8, (E, rows, K), generator=g, device=device, dtype=torch.uint8)
+        w[name + "_codes"] = (sign << 7) | (expo << 3) | mant
+        base = 127 - int(round(math.log2(math.sqrt(K)))) - 1
+        w[name + "_scales"] = (base + torch.randint(-1, 2, (E, rows, K // MX_BLOCK), generator=g,
+                                                    device=device)).to(torch.uint8)
+    bias = None
+    if shape.zipf_s is not None:
+        rank = torch.randperm(E, generator=g, device=device).to(torch.float64) + 1
+        bias = (-shape.zipf_s * torch.log(rank)).to(torch.float32)
+    return dict(w_router=w_router, logit_bias=bias, w=w)

@@ -28,4 +28,12 @@ from .moe_oracle import (  # noqa: F401
     dequantize_affine,
     forward_quantized,
     QUANT_GROUP,
+    MX_BLOCK,
+    e4m3_value,
+    e8m0_value,
+    e4m3_round,
+    mx_quantize,
+    mx_dequantize,
+    round_to_bf16_via_f32,
+    forward_mxfp8,
 )

@@ -340,3 +340,121 @@ def forward_quantized(layer: dict, tokens: np.ndarray | None = None) -> dict:
     w13 = DequantizedExperts(layer["w13_q"], layer["w13_scales"], layer["w13_biases"], bits, H)
     w2 = DequantizedExperts(layer["w2_q"], layer["w2_scales"], layer["w2_biases"], bits, I)
     return dict(route=r, tokens=tokens, y=layer_forward(x, w13, w2, ids, wts, tokens))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 experts and activations.  The MLX part of the page "SGLang issue
+# #22283" names MXFP8 next to the affine formats; the format is the OCP
+# Microscaling (MX) one: blocks of 32 consecutive elements along K, each
+# block one E8M0 scale (a power of two, 2^(code - 127)) and 32 FP8 E4M3
+# elements (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+# is subnormal, m * 2^-9; 0x7F and 0xFF are NaN; no infinities; largest
+# finite 448).  The page [MoE-vLLM] "The two index lists" names the FP8
+# GEMM 1 input qhidden, a quantized copy of x.
+# Readings: x (GEMM 1 input) and act (GEMM 2 input) are both quantized to
+# MXFP8 by the layer; act is the bf16 activation (fp32 value rounded to
+# bf16, as the bf16 layer stores it) before it is quantized; the router stays
+# bf16.  Quantizing a block: amax = max |v|; the scale is 2^(floor(log2
+# amax) - 8) (8 = the exponent of E4M3's largest power of two), clamped to
+# E8M0's range [2^-127, 2^127], code 0 for an all-zero block; an element is
+# v / scale rounded to the nearest E4M3 value, ties to the even code,
+# saturating at +-448; the sign of v is kept, also when it rounds to zero.
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """E4M3 code bytes -> float64 (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e8m0_value(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(code - 127) (NaN for 0xFF)."""
+    c = np.asarray(codes).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+_E4M3_GRID = e4m3_value(np.arange(0x7F))          # the 127 finite non-negative values, ascending
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of each finite float64 value, ties to the even
+    code, saturating at +-448, sign kept (also for a zero result)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(_E4M3_GRID, a, side="left"), 1, 0x7E)
+    lo = hi - 1
+    dlo = a - _E4M3_GRID[lo]
+    dhi = _E4M3_GRID[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    mag = np.where(pick_hi, hi, lo)
+    mag = np.where(a >= _E4M3_GRID[0x7E], 0x7E, mag)
+    return (mag | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mx_quantize(v: np.ndarray, block: int = MX_BLOCK) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 codes [..., K] (uint8 E4M3) and scales [..., K/32] (uint8 E8M0)
+    of float64 values [..., K] (K a multiple of 32)."""
+    v = np.asarray(v, dtype=np.float64)
+    blocks = v.reshape(*v.shape[:-1], v.shape[-1] // block, block)
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(amax)                      # amax = f * 2^ex, f in [0.5, 1)
+    shared = np.clip(ex - 1 - 8, -127, 127)     # floor(log2 amax) - 8
+    shared = np.where(amax == 0, -127, shared)
+    codes = e4m3_round(blocks / np.exp2(shared.astype(np.float64))[..., None])
+    return codes.reshape(v.shape), (shared + 127).astype(np.uint8)
+
+
+_E4M3_ALL = e4m3_value(np.arange(256))         # every code's value (a table of the same definition)
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, block: int = MX_BLOCK) -> np.ndarray:
+    """float64 values of MXFP8 codes [..., K] with scales [..., K/32]."""
+    c = _E4M3_ALL[np.asarray(codes, dtype=np.uint8)]
+    s = np.repeat(e8m0_value(scales), block, axis=-1)
+    return c * s
+
+
+def round_to_bf16_via_f32(v: np.ndarray) -> np.ndarray:
+    """bf16 bits of float64 values rounded first to float32 and then to
+    bf16, both to nearest even (an fp32 value stored as bf16)."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (f + 0x7FFF + ((f >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def forward_mxfp8(layer: dict, tokens: np.ndarray | None = None) -> dict:
+    """The layer with MXFP8 experts and activations (a dict made by
+    ``moe_workloads.make_mx_layer``): routing as ``forward`` (bf16 router),
+    x quantized to MXFP8, per pair h = W13_e deq(q(x_t)), act = SwiGLU(h)
+    stored as bf16 then quantized to MXFP8, y_p = W2_e deq(q(act_p)), and
+    the weighted top-k sum."""
+    x = layer["x"]
+    M, H = x.shape
+    I, k = layer["I"], layer["top_k"]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    r = route(x[tokens], layer["w_router"], k, layer["renormalize"], layer.get("logit_bias"))
+    ids = np.zeros((M, k), dtype=np.int32)
+    wts = np.zeros((M, k))
+    ids[tokens] = r["topk_ids"]
+    wts[tokens] = r["topk_weights"]
+    xq, xs = mx_quantize(widen_bf16(x))
+    X = mx_dequantize(xq, xs)
+    pos = np.full(M, -1)
+    pos[tokens] = np.arange(tokens.size)
+    slots = np.zeros((tokens.size, k, H))
+    for e, ts, js in _pairs_by_expert(ids, tokens):
+        W13 = mx_dequantize(layer["w13_codes"][e], layer["w13_scales"][e])
+        W2 = mx_dequantize(layer["w2_codes"][e], layer["w2_scales"][e])
+        act = widen_bf16(round_to_bf16_via_f32(swiglu(X[ts] @ W13.T, I)))
+        aq, asc = mx_quantize(act)
+        slots[pos[ts], js] = mx_dequantize(aq, asc) @ W2.T
+    y = np.einsum("tk,tkh->th", wts[tokens], slots)
+    return dict(route=r, tokens=tokens, y=y, x_codes=xq, x_scales=xs)
