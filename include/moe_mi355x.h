@@ -68,6 +68,8 @@ typedef enum moe_status {
                                     with no index lists, when M*top_k*4 <= E) */
 #define MOE_VARIANT_PAIR_GEMV_QUANT 3  /* moe_forward_quantized: per-pair GEMVs on
                                           group-quantized weights */
+#define MOE_VARIANT_TILED_MXFP8 4  /* moe_forward_mxfp8: LDS-tiled scaled-MFMA GEMMs on
+                                      MXFP8 operands */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -265,6 +267,62 @@ int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const flo
                           int renormalize, uint16_t* out, int32_t* topk_ids_out,
                           float* topk_weights_out, void* workspace, size_t ws_bytes,
                           moe_dispatch_info* info, void* stream);
+
+/*
+ * MXFP8 experts (the FP8 layer of page "Mixture of Experts in vLLM - From
+ * First Principles to fused_moe", sub-section "The two index lists": the
+ * GEMM 1 input qhidden is a quantized copy of x; the MXFP8 format named in
+ * the MLX part of the page "SGLang issue #22283"): the OCP microscaling
+ * format, blocks of 32 consecutive elements along K, each with one E8M0
+ * scale byte c (the value 2^(c - 127)) and 32 E4M3 bytes (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; 0x7F and 0xFF are NaN).  All arrays
+ * row-major, K contiguous, 16-byte aligned.
+ */
+typedef struct moe_mx_weights {
+  const uint8_t* w13_codes;    /* [E, 2I, H] E4M3                              */
+  const uint8_t* w13_scales;   /* [E, 2I, H/32] E8M0                           */
+  const uint8_t* w2_codes;     /* [E, H, I] E4M3                               */
+  const uint8_t* w2_scales;    /* [E, H, I/32] E8M0                            */
+} moe_mx_weights;
+
+/*
+ * moe_mx_quantize -- MXFP8 codes [rows, K] and scales [rows, K/32] of bf16
+ * rows src [rows, K] (K a multiple of 32; device pointers, src and codes
+ * 16-byte aligned).  Per block of 32: scale 2^(floor(log2 amax) - 8)
+ * clamped to [2^-127, 2^127] (code 0 for an all-zero block); element =
+ * v / scale rounded to the nearest E4M3 value, ties to the even code,
+ * saturated at 448, sign kept.  One launch; returns MOE_OK, or
+ * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED (K % 32) before any launch.
+ */
+int moe_mx_quantize(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
+                    void* stream);
+
+/* Workspace bytes for every moe_forward_mxfp8 call with M <= M_max (0 if
+ * the sizes are unsupported: H or I not a multiple of 128, or as for
+ * moe_workspace_size). */
+size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I);
+
+/*
+ * moe_forward_mxfp8 -- the layer of moe_forward with MXFP8 expert weights
+ * and MXFP8 GEMM inputs: routing on the bf16 router as moe_forward; x
+ * quantized to MXFP8 (moe_mx_quantize); GEMM 1 on the gfx950 scaled MFMA
+ * (E4M3 x E4M3, each 32-element block scaled by its E8M0 factor, fp32
+ * accumulation) with SiLU(gate)*up, act stored bf16; act quantized to
+ * MXFP8; GEMM 2 likewise into bf16 pair-order rows; the weighted top-k sum
+ * per token.  Index lists with block_m = moe_pick_block_m(M, E, top_k), at
+ * least 64 (the tiled kernels serve every batch size here).
+ *
+ *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, info,
+ *   stream: as for moe_forward;  w: host struct of device pointers
+ *   workspace: at least moe_mx_workspace_size(M, ...) bytes, 16-byte aligned
+ * H and I must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise).
+ * info->variant reads MOE_VARIANT_TILED_MXFP8.
+ */
+int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                      const moe_mx_weights* w, int M, int E, int top_k, int H, int I,
+                      int renormalize, uint16_t* out, int32_t* topk_ids_out,
+                      float* topk_weights_out, void* workspace, size_t ws_bytes,
+                      moe_dispatch_info* info, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ binding works but every call raises.
 
 Function names match the C ABI: moe_route, moe_align,
 moe_grouped_gemm_w13_act, moe_grouped_gemm_w2_combine, moe_forward,
-moe_forward_quantized, plus moe_workspace_size, moe_pick_block_m and
+moe_forward_quantized, moe_forward_mxfp8, moe_mx_quantize, plus
+moe_workspace_size, moe_mx_workspace_size, moe_pick_block_m and
 moe_strerror.
 """
 
@@ -25,6 +26,7 @@ MOE_VARIANT_TILED = 0
 MOE_VARIANT_STREAM = 1
 MOE_VARIANT_PAIR_GEMV = 2
 MOE_VARIANT_PAIR_GEMV_QUANT = 3
+MOE_VARIANT_TILED_MXFP8 = 4
 
 _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -44,6 +46,12 @@ class DispatchInfo(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class MxWeights(ctypes.Structure):
+    """moe_mx_weights: four device pointers (E4M3 codes and E8M0 scales)."""
+    _fields_ = [("w13_codes", _c_void_p), ("w13_scales", _c_void_p),
+                ("w2_codes", _c_void_p), ("w2_scales", _c_void_p)]
 
 
 class QuantizedWeights(ctypes.Structure):
@@ -71,6 +79,11 @@ _SIGNATURES = {
     "moe_forward": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
                     [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                      ctypes.POINTER(DispatchInfo), _c_void_p]),
+    "moe_mx_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_mx_workspace_size": (_c_size_t, [_c_int] * 5),
+    "moe_forward_mxfp8": (_c_int, [_c_void_p] * 3 + [ctypes.POINTER(MxWeights)] + [_c_int] * 6 +
+                          [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                           ctypes.POINTER(DispatchInfo), _c_void_p]),
     "moe_forward_quantized": (_c_int, [_c_void_p] * 3 + [ctypes.POINTER(QuantizedWeights)] +
                               [_c_int] * 6 +
                               [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
@@ -364,4 +377,71 @@ def moe_forward_quantized(x, w_router, qweights: dict, top_k: int, renormalize: 
         int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
         _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
     _raise("moe_forward_quantized", st)
+    return out, info.as_dict()
+
+
+def moe_mx_workspace_size(M_max: int, E: int, top_k: int, H: int, I: int) -> int:
+    return int(library().moe_mx_workspace_size(M_max, E, top_k, H, I))
+
+
+def mx_workspace(M_max: int, E: int, top_k: int, H: int, I: int, device=None):
+    """Workspace tensor (uint8) for every moe_forward_mxfp8 call with M <= M_max."""
+    torch = _torch()
+    n = moe_mx_workspace_size(M_max, E, top_k, H, I)
+    if n == 0:
+        raise MoeError("moe_mx_workspace_size", -2)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_mx_quantize(src, codes=None, scales=None, stream=None):
+    """MXFP8 codes [rows, K] (uint8 E4M3) and scales [rows, K/32] (uint8
+    E8M0) of bf16 rows src [rows, K]."""
+    torch = _torch()
+    rows, K = src.shape
+    _check(src, "src", _bf16_types())
+    if codes is None:
+        codes = torch.empty((rows, K), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=src.device)
+    _check(codes, "codes", (torch.uint8,), (rows, K))
+    _check(scales, "scales", (torch.uint8,), (rows, K // 32))
+    st = library().moe_mx_quantize(_ptr(src), rows, K, _ptr(codes), _ptr(scales), _stream(stream))
+    _raise("moe_mx_quantize", st)
+    return codes, scales
+
+
+def moe_forward_mxfp8(x, w_router, mxw: dict, top_k: int, renormalize: bool = True,
+                      logit_bias=None, out=None, topk_ids_out=None, topk_weights_out=None,
+                      ws=None, stream=None):
+    """The layer with MXFP8 experts and GEMM inputs.  ``mxw`` holds
+    ``w13_codes`` [E, 2I, H], ``w13_scales`` [E, 2I, H/32], ``w2_codes``
+    [E, H, I] and ``w2_scales`` [E, H, I/32] (uint8).  Returns (out [M, H]
+    bf16, dispatch info dict)."""
+    torch = _torch()
+    M, H = x.shape
+    E = w_router.shape[0]
+    I = mxw["w2_codes"].shape[2]
+    _check(x, "x", _bf16_types())
+    _check(w_router, "w_router", _bf16_types(), (E, H))
+    for name, shape in (("w13_codes", (E, 2 * I, H)), ("w13_scales", (E, 2 * I, H // 32)),
+                        ("w2_codes", (E, H, I)), ("w2_scales", (E, H, I // 32))):
+        _check(mxw[name], name, (torch.uint8,), shape)
+    if logit_bias is not None:
+        _check(logit_bias, "logit_bias", (torch.float32,), (E,))
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", _bf16_types(), (M, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", (torch.int32,), (M, top_k))
+    if topk_weights_out is not None:
+        _check(topk_weights_out, "topk_weights_out", (torch.float32,), (M, top_k))
+    if ws is None:
+        ws = mx_workspace(M, E, top_k, H, I, x.device)
+    w = MxWeights(*(_ptr(mxw[n]) for n in ("w13_codes", "w13_scales", "w2_codes", "w2_scales")))
+    info = DispatchInfo()
+    st = library().moe_forward_mxfp8(
+        _ptr(x), _ptr(w_router), _ptr(logit_bias), ctypes.byref(w), M, E, top_k, H, I,
+        int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
+        _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
+    _raise("moe_forward_mxfp8", st)
     return out, info.as_dict()

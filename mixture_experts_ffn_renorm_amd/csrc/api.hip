@@ -426,3 +426,134 @@ int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const flo
 }
 
 }  // extern "C"
+
+// ---- MXFP8 layer ----
+
+namespace {
+
+struct MxLayout {
+  Layout base;
+  size_t qx, sx, qact, sact, total;
+};
+
+int mx_block_m(int M, int E, int top_k) {
+  const int B = moe_pick_block_m(M, E, top_k);
+  return B < 64 ? 64 : B;
+}
+
+MxLayout mx_layout(int M, int E, int top_k, int H, int I, int B) {
+  MxLayout L;
+  L.base = forward_layout(M, E, top_k, H, I, B);
+  const size_t P = (size_t)M * top_k;
+  size_t off = L.base.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.qx = take((size_t)M * H);
+  L.sx = take((size_t)M * H / 32);
+  L.qact = take(P * I);
+  L.sact = take(P * I / 32);
+  L.total = off;
+  return L;
+}
+
+bool mx_sizes_ok(int H, int I) { return H % 128 == 0 && I % 128 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_mx_quantize(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
+                    void* stream) {
+  if (rows < 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!src || !codes || !scales || !a16(src) || !a16(codes)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY_HIP(launch_mx_quantize(src, rows, K, codes, scales, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I) {
+  if (check_sizes(M_max, E, top_k, H, I) != MOE_OK || !mx_sizes_ok(H, I)) return 0;
+  size_t best = 0;
+  for (int B : {64, 128, 256}) best = std::max(best, mx_layout(M_max, E, top_k, H, I, B).total);
+  return std::max<size_t>(best, kAlign);
+}
+
+int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                      const moe_mx_weights* w, int M, int E, int top_k, int H, int I,
+                      int renormalize, uint16_t* out, int32_t* topk_ids_out,
+                      float* topk_weights_out, void* workspace, size_t ws_bytes,
+                      moe_dispatch_info* info, void* stream) {
+  int st = check_sizes(M, E, top_k, H, I);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (w == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!mx_sizes_ok(H, I)) return MOE_ERR_UNSUPPORTED;
+  const int B = mx_block_m(M, E, top_k);
+  const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
+  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 2 + 2 + kGemm2Launches);
+  if (info != nullptr) info->variant = MOE_VARIANT_TILED_MXFP8;
+  if (M == 0) return MOE_OK;
+  if (!x || !w_router || !out || !w->w13_codes || !w->w13_scales || !w->w2_codes ||
+      !w->w2_scales)
+    return MOE_ERR_INVALID_ARG;
+  if (!a16(x) || !a16(w_router) || !a16(out) || !a16(workspace) || !a16(w->w13_codes) ||
+      !a16(w->w2_codes) || !a16(w->w13_scales) || !a16(w->w2_scales))
+    return MOE_ERR_INVALID_ARG;
+  const MxLayout X = mx_layout(M, E, top_k, H, I, B);
+  const Layout& L = X.base;
+  if (workspace == nullptr || ws_bytes < X.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(ws + L.wts);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(ws + L.eids);
+  int32_t* boff = reinterpret_cast<int32_t*>(ws + L.boff);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+  uint8_t* qx = reinterpret_cast<uint8_t*>(ws + X.qx);
+  uint8_t* sx = reinterpret_cast<uint8_t*>(ws + X.sx);
+  uint8_t* qact = reinterpret_cast<uint8_t*>(ws + X.qact);
+  uint8_t* sact = reinterpret_cast<uint8_t*>(ws + X.sact);
+
+  RouteArgs ra{x, w_router, logit_bias, M, H, E, top_k, renormalize,
+               reinterpret_cast<float*>(ws + L.logits), ids, wts,
+               reinterpret_cast<float*>(ws + L.arrive), 1};
+  AlignArgs aa{ids, M * top_k, E, B, sorted, eids, boff,
+               reinterpret_cast<int32_t*>(ws + L.counts),
+               reinterpret_cast<int32_t*>(ws + L.align_scratch)};
+  MOE_TRY_HIP(launch_route_logits(ra, s));
+  if (fused_route(M, top_k)) {
+    MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive), s));
+  } else {
+    MOE_TRY_HIP(launch_route_topk(ra, s));
+    MOE_TRY_HIP(launch_align(aa, s));
+  }
+  MOE_TRY_HIP(launch_mx_quantize(x, M, H, qx, sx, s));
+  GemmArgs g = gemm_args(M, top_k, E, H, I, B);
+  g.sorted_token_ids = sorted;
+  g.expert_ids = eids;
+  g.expert_block_offsets = boff;
+  g.mx = 1;
+  g.a_src = reinterpret_cast<const uint16_t*>(qx);
+  g.a_scales = sx;
+  g.w = reinterpret_cast<const uint16_t*>(w->w13_codes);
+  g.w_scales = w->w13_scales;
+  g.out = act;
+  MOE_TRY_HIP(launch_gemm1_tiled(g, s));
+  MOE_TRY_HIP(launch_mx_quantize(act, M * top_k, I, qact, sact, s));
+  g.a_src = reinterpret_cast<const uint16_t*>(qact);
+  g.a_scales = sact;
+  g.w = reinterpret_cast<const uint16_t*>(w->w2_codes);
+  g.w_scales = w->w2_scales;
+  g.topk_weights = wts;
+  g.out = out;
+  g.partial = reinterpret_cast<float*>(ws + L.partial);
+  MOE_TRY_HIP(launch_gemm2_tiled(g, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

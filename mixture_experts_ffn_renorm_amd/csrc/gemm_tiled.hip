@@ -35,6 +35,18 @@
 // one finishes and runs its epilogue.  A tile's pair ids and expert id are
 // copied into LDS by the same asynchronous copies two tiles ahead.
 //
+// MXFP8 operands (kMX; OCP microscaling: E4M3 bytes, one E8M0 scale per 32
+// consecutive k): the same 128-byte row pieces, now 128 k values each, so a
+// stage is one k step of the gfx950 scaled MFMA 16x16x128.  That MFMA reads
+// from lane (r, g) the 16 bytes at k 16g .. 16g + 15 and the 16 bytes at
+// 64 + 16g .. (measured with in-bounds probes: byte i of lane group g sits
+// at k 64 (i / 16) + 16 g + i % 16, E4M3 as OCP defines it), which are
+// exactly the two 16-byte chunks g and 4 + g the bf16 form reads for its
+// two k halves, and takes the scale of k block s (32 values) of row r from
+// lane r + 16 s.  Each stage also copies 4 scale bytes per row (the stage's
+// four blocks) into an LDS area after the operands, one 4-byte copy per
+// lane: 512 rows, the ones past the tile reading the zeroed page.
+//
 // Copies go from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging).  One copy instruction of a
 // wave fills 1 KB of LDS = 8 rows of 64 k values; a row's eight 16-byte
@@ -60,15 +72,18 @@ constexpr int kMeta = 5;         // tile metadata buffers (pair ids, expert)
 
 // Tile shape per block size BM: 256 weight rows x BM pairs, waves in a
 // 4 (features, 64 rows each) x 2 (pair halves) layout.
-template <int BM>
+template <int BM, bool kMX = false>
 struct TileCfg {
   static constexpr int kBN = 256;                      // weight rows per tile
   static constexpr int kWF = kBN / 64;
   static constexpr int kWP = kWaves / kWF;
   static constexpr int kWGroups = kBN / 8 / kWaves;   // 8-row W groups per wave (2 or 4)
   static constexpr int kXGroups = BM / 8 / kWaves;    // 8-row X groups per wave (1, 2 or 4)
-  static constexpr int kLoads = kWGroups + kXGroups;  // copy instructions per stage
-  static constexpr int kStageBytes = (kBN + BM) * kRowBytes;   // 40, 48 or 64 KB
+  // copy instructions per stage (MX: one more, the scales)
+  static constexpr int kLoads = kWGroups + kXGroups + (kMX ? 1 : 0);
+  static constexpr int kOperandBytes = (kBN + BM) * kRowBytes;       // 40, 48 or 64 KB
+  static constexpr int kScaleRows = kWaves * 64;                     // MX: 4 bytes each
+  static constexpr int kStageBytes = kOperandBytes + (kMX ? kScaleRows * 4 : 0);
   static constexpr int kStages = BM == 256 ? 2 : 3;    // ring within 160 KB of LDS
   static constexpr int kRingBytes = kStages * kStageBytes;
   static constexpr int kNT = BM / kWP / 16;           // 16-pair MFMA tiles per wave
@@ -81,14 +96,29 @@ struct TileCfg {
 // stride, or the XOR with (R ^ (R >> 3)) & 7, both run at about half).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 cat_u32x4(u32x4 lo, u32x4 hi) {
+  const u32x4 l = lo, h = hi;   // by value
+  return i32x8{(int)l[0], (int)l[1], (int)l[2], (int)l[3], (int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+}
+
+// D = A B + C over 128 k of E4M3 operands, each lane's 32 values scaled by
+// 2^(its E8M0 byte - 127) (format code 0 = E4M3 for both operands).
+__device__ __forceinline__ f32x4 mfma_mx_16x16x128(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // Each active lane copies 4 bytes from src to LDS at lds_dst + 4 * lane.
 __device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 4, 0, 0);
 }
 
 struct TileParams {
-  const uint16_t* a_src;   // GEMM 1: x [M, H]; GEMM 2: act [P, I]
+  const uint16_t* a_src;   // GEMM 1: x [M, H]; GEMM 2: act [P, I]  (MX: E4M3 bytes)
   const uint16_t* w;       // GEMM 1: w13 [E, 2I, H]; GEMM 2: w2 [E, H, I]
+  const uint8_t* a_scales; // MX: E8M0 per 32 k of each a_src row
+  const uint8_t* w_scales; // MX: E8M0 per 32 k of each weight row
   const int32_t* sorted;
   const int32_t* expert_ids;
   const int32_t* boff;
@@ -97,9 +127,9 @@ struct TileParams {
   uint16_t* out;           // GEMM 1: act [P, I]; GEMM 2: pair-order product [P, H]
 };
 
-template <int BM, bool kGemm1>
+template <int BM, bool kGemm1, bool kMX>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParams prm) {
-  using C = TileCfg<BM>;
+  using C = TileCfg<BM, kMX>;
   constexpr int NT = C::kNT;
   constexpr int kStages = C::kStages;
   constexpr int kBN = C::kBN;
@@ -109,7 +139,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   __shared__ int s_exp[kMeta];
 
   const int P = prm.M * prm.top_k;
-  const int K = kGemm1 ? prm.H : prm.I;
+  const int Ke = kGemm1 ? prm.H : prm.I;   // k elements
+  const int K = kMX ? Ke / 2 : Ke;          // k in 2-byte units (MX: Ke % 128 == 0)
   const int ntn = prm.ntn;
   const int njobs = prm.boff[prm.E] * ntn;
   // tiles of this workgroup: j0, j0 + nslots, ... inside its XCD's range
@@ -142,6 +173,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   int wstep[C::kWGroups], xstep[C::kXGroups];
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroPage);
   const bool k_tail = (K % kBK) != 0;
+  // MX: this lane copies the 4 scale bytes of row 64 wv + lane of the tile
+  // (weight rows, then pair rows, then unused) for each stage
+  const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(kZeroPage);
+  int sstep = 0;
 
   // Point the copy sources at tile i (its metadata is in LDS), and start the
   // metadata copies of tile i + 2.
@@ -171,10 +206,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
       const int p = s_pair[buf][R];
       const uint16_t* row = nullptr;
       if (p < P)
-        row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * prm.H
-                     : prm.a_src + (size_t)p * prm.I;
+        row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * K    // K: row length in
+                     : prm.a_src + (size_t)p * K;                 // 2-byte units
       xsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
       xstep[gi] = row != nullptr ? kBK : 0;
+    }
+    if constexpr (kMX) {
+      const int R = wv * 64 + lane, nb = Ke / 32;
+      const uint8_t* srow = nullptr;
+      if (R < kBN) {
+        if (kGemm1) {
+          const int f = nt * kHalf + (R % kHalf);
+          if (f < prm.I)
+            srow = prm.w_scales + ((size_t)e * 2 * prm.I + (R < kHalf ? f : prm.I + f)) * nb;
+        } else {
+          const int h = nt * kBN + R;
+          if (h < prm.H) srow = prm.w_scales + ((size_t)e * prm.H + h) * nb;
+        }
+      } else if (R < kBN + BM) {
+        const int p = s_pair[buf][R - kBN];
+        if (p < P)
+          srow = prm.a_scales + (size_t)(kGemm1 ? p / prm.top_k : p) * nb;
+      }
+      ssrc = srow != nullptr ? srow : reinterpret_cast<const uint8_t*>(kZeroPage);
+      sstep = srow != nullptr ? 4 : 0;
     }
     issue_meta(i + 2);
   };
@@ -202,6 +257,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
       if (tail && (lpos ^ swz((wv + kWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
       load_lds16(src, sb + (kBN + (wv + kWaves * gi) * 8) * kRowBytes);
       xsrc[gi] += xstep[gi];
+    }
+    if constexpr (kMX) {
+      load_lds4(ssrc, sb + C::kOperandBytes + wv * 256);
+      ssrc += sstep;
     }
   };
 
@@ -248,6 +307,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     if (g < G) issue_stage();
 
   bool act0 = true, act1 = true;   // this wave's quarters hold a pair
+  // MX: one scaled MFMA per (A tile, B tile) per stage; the lane's operand
+  // is chunks kg and 4 + kg of its row, its scale byte that of k block kg.
+  auto compute_mx = [&](const uint8_t* sb) {
+    const uint8_t* sc = sb + C::kOperandBytes;
+    i32x8 af[4];
+    int sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = cat_u32x4(*reinterpret_cast<const u32x4*>(sb + abase[0] + aconst(i)),
+                        *reinterpret_cast<const u32x4*>(sb + abase[1] + aconst(i)));
+      const int row = arow0 + (kGemm1 ? (i >> 1) * kHalf + (i & 1) * 16 : 16 * i) + r16;
+      sa[i] = sc[row * 4 + kg];
+    }
+    // B tiles one at a time (the A tiles stay in registers)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!(q == 0 ? act0 : act1)) continue;
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) {
+        const int off = (q * 2 * QS + 16 * j) * kRowBytes;
+        const i32x8 bfr = cat_u32x4(*reinterpret_cast<const u32x4*>(sb + bbase[0] + off),
+                                    *reinterpret_cast<const u32x4*>(sb + bbase[1] + off));
+        const int sbv = sc[(kBN + wp * QS + q * 2 * QS + 16 * j + r16) * 4 + kg];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][q * TQ + j] = mfma_mx_16x16x128(af[i], bfr, acc[i][q * TQ + j], sa[i], sbv);
+      }
+    }
+  };
   // One stage of MFMAs over this wave's active quarters, fully unrolled.
   auto compute = [&](const uint8_t* sb) {
 #pragma unroll
@@ -288,7 +376,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
       act1 = __ballot(v1) != 0ull;
     }
     const uint8_t* sb = ring + c_slot * C::kStageBytes;
-    if (act0 || act1) compute(sb);
+    if (act0 || act1) {
+      if constexpr (kMX) compute_mx(sb); else compute(sb);
+    }
     c_slot = c_slot == kStages - 1 ? 0 : c_slot + 1;
     if (++c_kt == nk) { c_kt = 0; ++c_i; c_buf = c_buf == kMeta - 1 ? 0 : c_buf + 1; }
     if (kt != nk - 1) continue;
@@ -363,12 +453,14 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __res
   *reinterpret_cast<u32x4*>(out + (size_t)t * H + h) = o;
 }
 
-template <int BM, bool kGemm1>
+template <int BM, bool kGemm1, bool kMX = false>
 hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* out) {
-  constexpr int kBN = TileCfg<BM>::kBN;
+  constexpr int kBN = TileCfg<BM, kMX>::kBN;
   TileParams prm;
   prm.a_src = a.a_src;
   prm.w = a.w;
+  prm.a_scales = a.a_scales;
+  prm.w_scales = a.w_scales;
   prm.sorted = a.sorted_token_ids;
   prm.expert_ids = a.expert_ids;
   prm.boff = a.expert_block_offsets;
@@ -383,16 +475,16 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* ou
   const long long tiles = (long long)a.max_blocks * prm.ntn;
   long long grid = std::min<long long>(tiles, moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
-  const size_t lds = TileCfg<BM>::kRingBytes;
+  const size_t lds = TileCfg<BM, kMX>::kRingBytes;
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1>),
+        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1>), dim3((unsigned)grid), dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX>), dim3((unsigned)grid), dim3(kThreads), lds, s,
                      prm);
   return hipGetLastError();
 }
@@ -402,6 +494,11 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* ou
 namespace moe_host {
 
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s) {
+  if (a.mx) {
+    if (a.block_m == 256) return launch_tiled<256, true, true>(a, s, a.out);
+    if (a.block_m == 128) return launch_tiled<128, true, true>(a, s, a.out);
+    return launch_tiled<64, true, true>(a, s, a.out);
+  }
   if (a.block_m == 256) return launch_tiled<256, true>(a, s, a.out);
   if (a.block_m == 128) return launch_tiled<128, true>(a, s, a.out);
   return launch_tiled<64, true>(a, s, a.out);
@@ -409,9 +506,15 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
   uint16_t* rows = reinterpret_cast<uint16_t*>(a.partial);
-  hipError_t err = a.block_m == 256   ? launch_tiled<256, false>(a, s, rows)
-                    : a.block_m == 128 ? launch_tiled<128, false>(a, s, rows)
-                                       : launch_tiled<64, false>(a, s, rows);
+  hipError_t err;
+  if (a.mx)
+    err = a.block_m == 256   ? launch_tiled<256, false, true>(a, s, rows)
+          : a.block_m == 128 ? launch_tiled<128, false, true>(a, s, rows)
+                             : launch_tiled<64, false, true>(a, s, rows);
+  else
+    err = a.block_m == 256   ? launch_tiled<256, false>(a, s, rows)
+          : a.block_m == 128 ? launch_tiled<128, false>(a, s, rows)
+                             : launch_tiled<64, false>(a, s, rows);
   if (err != hipSuccess) return err;
   const long long n8 = (long long)a.M * (a.H / 8);
   hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, rows,

@@ -344,7 +344,13 @@ struct GemmArgs {
   uint16_t* out;             // GEMM 1: act [P, I]; GEMM 2: out [M, H]
   float* partial;            // GEMM 2: pair-order rows [P, H], fp32 weighted
                              // (streaming) or bf16 (tiled)
+  int mx;                    // tiled only: a_src and w hold MXFP8 E4M3 bytes
+  const uint8_t* a_scales;   // MX: E8M0 per 32 k of each a_src row
+  const uint8_t* w_scales;   // MX: E8M0 per 32 k of each weight row
 };
+// MXFP8 codes [rows, K] and E8M0 scales [rows, K/32] of bf16 rows (K % 32 == 0).
+hipError_t launch_mx_quantize(const uint16_t* src, int rows, int K, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s);

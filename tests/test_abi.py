@@ -181,3 +181,38 @@ def test_forward_quantized_null_struct_and_workspace():
     qw = moe.QuantizedWeights(4, 64, *([0x10000] * 6))
     assert lib.moe_forward_quantized(fake, fake, NULL, ctypes.byref(qw), 4, 128, 8, 2048, 768, 1,
                                      fake, NULL, NULL, fake, 1024, NULL, NULL) == -3
+
+
+@pytest.mark.parametrize("H,I,M,status", [
+    (2048, 768, 4, -1),          # null pointers
+    (2048 + 64, 768, 4, -2),     # H % 128
+    (2048, 768 + 32, 4, -2),     # I % 128
+    (2048, 768, 0, 0),           # M = 0: no launch
+])
+def test_forward_mxfp8_argument_checks(H, I, M, status):
+    moe = _moe()
+    lib = moe.library()
+    w = moe.MxWeights()
+    info = moe.DispatchInfo()
+    st = lib.moe_forward_mxfp8(NULL, NULL, NULL, ctypes.byref(w), M, 128, 8, H, I, 1, NULL, NULL,
+                               NULL, NULL, 0, ctypes.byref(info), NULL)
+    assert st == status
+    if status == 0:
+        assert info.variant == moe.MOE_VARIANT_TILED_MXFP8 and info.launches == 0
+        assert info.block_m == 64
+
+
+def test_mx_workspace_and_quantize_checks():
+    moe = _moe()
+    lib = moe.library()
+    assert moe.moe_mx_workspace_size(64, 128, 8, 2048, 768) >= moe.moe_workspace_size(64, 128, 8, 2048, 768)
+    assert moe.moe_mx_workspace_size(64, 128, 8, 2048 + 64, 768) == 0
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.moe_mx_quantize(fake, 4, 48, fake, fake, NULL) == -2        # K % 32
+    assert lib.moe_mx_quantize(NULL, 4, 64, fake, fake, NULL) == -1
+    assert lib.moe_mx_quantize(NULL, 0, 64, NULL, NULL, NULL) == 0
+    assert lib.moe_forward_mxfp8(NULL, NULL, NULL, NULL, 4, 128, 8, 2048, 768, 1, NULL, NULL,
+                                 NULL, NULL, 0, NULL, NULL) == -1
+    w = moe.MxWeights(*([0x10000] * 4))
+    assert lib.moe_forward_mxfp8(fake, fake, NULL, ctypes.byref(w), 4, 128, 8, 2048, 768, 1, fake,
+                                 NULL, NULL, fake, 1024, NULL, NULL) == -3

@@ -1,0 +1,132 @@
+"""Parity of the MXFP8 path (moe_mx_quantize, moe_forward_mxfp8) against the
+oracle's mx_quantize and forward_mxfp8.
+
+* The quantizer is integer output decided by floating point on the same
+  exact values on both sides (division by a power of two), so its codes and
+  scales must match bit for bit: random blocks over a wide range of
+  magnitudes, all-zero blocks, negative zeros, exact ties between E4M3
+  neighbours, blocks that saturate at 448.
+* The layer: routing ids where the top-k margin exceeds 1e-4, weights to
+  1e-5, outputs within 2e-2 max-abs (relative to max |ref|) and 5e-3
+  mean-relative, on a small ragged layer, the Qwen3-30B-A3B decode shape
+  (64 tokens), the Qwen1.5-MoE shape (I = 1408 = 11 * 128) and the Qwen3
+  prefill shape with its Zipf prior (block_m 256), plus a poisoned
+  workspace.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import moe_workloads as wl
+from oracle import moe_oracle as mo
+from tests import helpers as h
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import mixture_experts_ffn_renorm_amd as moe
+    return moe
+
+
+def dev_u8(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda")
+
+
+def _quant_inputs(rows: int, K: int, seed: int) -> np.ndarray:
+    """bf16 bits: per block a random magnitude, some zero blocks, negative
+    zeros, exact ties, saturating blocks."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, K)) * np.repeat(
+        np.exp2(rng.integers(-30, 30, (rows, K // 32))), 32, axis=1)
+    v[0, :32] = 0.0
+    v[0, 32:64] = -0.0
+    bits = wl.f32_to_bf16_bits(v.astype(np.float32))
+    if rows > 2 and K >= 64:
+        # exact ties: block max 256 (scale 1), midpoints of E4M3 neighbours
+        grid = mo.e4m3_value(np.arange(0x7F))
+        mids = (grid[1:] + grid[:-1]) / 2
+        row = np.concatenate([[256.0], mids[rng.integers(0, mids.size, 31)],
+                              [448.0], [470.0, 500.0, -511.0], rng.standard_normal(28) * 300])
+        bits[1, :64] = wl.f32_to_bf16_bits(row.astype(np.float32))
+    return bits
+
+
+@pytest.mark.parametrize("rows,K,seed", [(37, 96, 1), (64, 2048, 2), (300, 768, 3)])
+def test_mx_quantize_bit_exact(rows, K, seed):
+    moe = _moe()
+    bits = _quant_inputs(rows, K, seed)
+    codes, scales = moe.moe_mx_quantize(h.dev_bf16(bits))
+    import torch
+    torch.cuda.synchronize()
+    ref_c, ref_s = mo.mx_quantize(mo.widen_bf16(bits))
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != ref_c)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+def mx_to_device(lay: dict) -> dict:
+    return {k: dev_u8(lay[k]) for k in ("w13_codes", "w13_scales", "w2_codes", "w2_scales")}
+
+
+def run_mx(lay: dict, ws=None, out=None):
+    import torch
+    moe = _moe()
+    M, k = lay["M"], lay["top_k"]
+    ids = torch.full((M, k), -1, dtype=torch.int32, device="cuda")
+    wts = torch.full((M, k), -1.0, dtype=torch.float32, device="cuda")
+    lb = None if lay.get("logit_bias") is None else h.dev_f32(lay["logit_bias"])
+    out, info = moe.moe_forward_mxfp8(h.dev_bf16(lay["x"]), h.dev_bf16(lay["w_router"]),
+                                      mx_to_device(lay), k, lay["renormalize"], logit_bias=lb,
+                                      out=out, topk_ids_out=ids, topk_weights_out=wts, ws=ws)
+    torch.cuda.synchronize()
+    return out, ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64), info
+
+
+def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
+    moe = _moe()
+    print(f"mxfp8 case {lay['name']} M={lay['M']} E={lay['E']} k={lay['top_k']} "
+          f"H={lay['H']} I={lay['I']}", flush=True)
+    out, ids, wts, info = run_mx(lay, **kw)
+    assert info["variant"] == moe.MOE_VARIANT_TILED_MXFP8
+    assert info["block_m"] == max(64, moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"]))
+    toks = h.sample_tokens(lay["M"], n_tokens, seed)
+    ref = mo.forward_mxfp8(lay, tokens=toks)
+    r = ref["route"]
+    ok = r["margin"] > h.MARGIN
+    assert ok.mean() >= 0.8
+    assert np.array_equal(ids[toks][ok], r["topk_ids"][ok])
+    assert np.abs(wts[toks][ok] - r["topk_weights"][ok]).max() <= h.WEIGHT_TOL
+    y = h.host_bf16_to_f64(out)[toks]
+    h.assert_close_outputs(y[ok], ref["y"][ok], "mxfp8 output")
+    return out
+
+
+MX_CASES = [("toy", 5, dict(E=8, top_k=2, H=256, I=128)),
+            ("toy", 70, dict(E=6, top_k=2, H=384, I=256)),
+            ("qwen3_decode", 64, {}),
+            ("qwen15", 512, {}),
+            ("qwen3_prefill", 4096, {})]
+
+
+@pytest.mark.parametrize("name,M,kw", MX_CASES, ids=lambda v: str(v))
+def test_forward_mxfp8(name, M, kw):
+    lay = wl.make_mx_layer(name, M, seed=500 + M if kw else None, **kw)
+    check_mx(lay, n_tokens=24 if M >= 512 else 48)
+
+
+def test_forward_mxfp8_poisoned_workspace():
+    """NaN-filled workspace and output give the same bits as a fresh call."""
+    import torch
+    moe = _moe()
+    lay = wl.make_mx_layer("toy", 70, E=6, top_k=2, H=384, I=256, seed=77)
+    ref_out = check_mx(lay).clone()
+    ws = moe.mx_workspace(70, 6, 2, 384, 256)
+    ws.fill_(0xFF)
+    out = torch.full((70, 384), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got, _, _, _ = run_mx(lay, ws=ws, out=out)
+    assert torch.equal(got.view(torch.int16), ref_out.view(torch.int16))
