@@ -14,6 +14,8 @@ Prints ONE JSON line:
                    runs on), against the MI355X peak
   cpu_baseline     the CPU oracle on a bounded sample of the same workload
   kernels          mean duration of every kernel of the step (events)
+  mxfp8            context: moe_forward_mxfp8 (MXFP8 experts and GEMM inputs)
+                   on the same shape and batch, the L layers drawn as MXFP8
   quantized        context: moe_forward_quantized (affine 64-element groups,
                    4 and 8 bits) on the same shape at M = 1 and 4, one captured
                    HIP graph of the L layers replayed
@@ -37,11 +39,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA, TFLOP/s
 
 DEFAULT_WORKLOAD = ("qwen3_decode", 64)
 
 
-VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant"}
+VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8"}
 
 
 def parse_args():
@@ -60,6 +63,8 @@ def parse_args():
                     help="skip the group-quantized (4- and 8-bit) small-batch figures")
     ap.add_argument("--quant-sizes", default="4:1,4:4,8:1,8:4",
                     help="bits:M pairs of the quantized figures (default 4:1,4:4,8:1,8:4)")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the MXFP8 figures")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration runs)")
     return ap.parse_args()
@@ -346,6 +351,10 @@ def main():
                            "layer_tokens_per_s_graph": round(M * L / graph_s, 1)}
         del graph, stack
 
+    # ---- MXFP8 experts and GEMM inputs at the same batch (context) ----
+    if not args.no_mx and H % 128 == 0 and I % 128 == 0:
+        result["mxfp8"] = mxfp8_figures(shape, M, L, x, dev, max(5, min(args.steps, 50)))
+
     # ---- group-quantized expert weights at small batches (context) ----
     if not args.no_quant and shape.H % 64 == 0 and shape.I % 64 == 0 and M <= 64:
         sizes = [tuple(int(v) for v in p.split(":")) for p in args.quant_sizes.split(",") if p]
@@ -367,6 +376,59 @@ def quantized_alg_bytes(shape, M, bits, touched):
     E, H, I = shape.E, shape.H, shape.I
     per_expert = 3 * H * I * bits // 8 + (3 * H * I // 64) * 4
     return touched * per_expert + 2 * E * H + 4 * M * H
+
+
+def mxfp8_figures(shape, M, L, x, dev, reps):
+    """moe_forward_mxfp8 on the workload's batch over L device-drawn MXFP8
+    layers, the L calls captured once into a HIP graph and replayed `reps`
+    times.  Algorithmic bytes: per touched expert 3*H*I E4M3 bytes and
+    3*H*I/32 scale bytes, the bf16 router, x in and out; flops as the bf16
+    layer (the GEMMs run at the fp8 rate)."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as wl
+    import mixture_experts_ffn_renorm_amd as moe
+
+    E, k, H, I = shape.E, shape.top_k, shape.H, shape.I
+    layers = [wl.make_device_mx_layer(shape, M, layer=i + 1, device=dev) for i in range(L)]
+    ws = moe.mx_workspace(M, E, k, H, I, dev)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ids = [torch.empty((M, k), dtype=torch.int32, device=dev) for _ in range(L)]
+
+    def run_all():
+        for i, lay in enumerate(layers):
+            _, info = moe.moe_forward_mxfp8(x, lay["w_router"], lay["w"], k, shape.renormalize,
+                                            logit_bias=lay["logit_bias"], out=out,
+                                            topk_ids_out=ids[i], ws=ws)
+        return info
+
+    info = run_all()
+    torch.cuda.synchronize()
+    touched = float(np.mean([torch.unique(t).numel() for t in ids]))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / (reps * L)
+    alg = touched * (3 * H * I + 3 * H * I // 32) + 2 * E * H + 4 * M * H
+    flops = 6 * H * I * M * k
+    del graph, layers
+    return {"M": M, "us_per_layer": round(us, 2), "tokens_per_s": round(M / (us * 1e-6), 1),
+            "alg_bytes": int(alg), "alg_flops": int(flops),
+            "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac_fp8": round(flops / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "mean_touched_experts": touched, "variant": VARIANT_NAMES[info["variant"]],
+            "block_m": info["block_m"], "launches": info["launches"]}
 
 
 def quantized_figures(shape, L, x, dev, reps, sizes):
