@@ -44,7 +44,8 @@ FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA, TFLOP/s
 DEFAULT_WORKLOAD = ("qwen3_decode", 64)
 
 
-VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8"}
+VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8",
+                 5: "stream_mxfp8"}
 
 
 def parse_args():

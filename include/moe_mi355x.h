@@ -70,6 +70,8 @@ typedef enum moe_status {
                                           group-quantized weights */
 #define MOE_VARIANT_TILED_MXFP8 4  /* moe_forward_mxfp8: LDS-tiled scaled-MFMA GEMMs on
                                       MXFP8 operands */
+#define MOE_VARIANT_STREAM_MXFP8 5  /* moe_forward_mxfp8: weight-streaming scaled-MFMA
+                                       GEMMs on MXFP8 operands (block_m 16) */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -310,13 +312,14 @@ size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I);
  * accumulation) with SiLU(gate)*up, act stored bf16; act quantized to
  * MXFP8; GEMM 2 likewise into bf16 pair-order rows; the weighted top-k sum
  * per token.  Index lists with block_m = moe_pick_block_m(M, E, top_k), at
- * least 64 (the tiled kernels serve every batch size here).
+ * least 16: weight-streaming kernels at block_m 16 (small batches, also the
+ * per-pair case), tiled kernels above.
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, info,
  *   stream: as for moe_forward;  w: host struct of device pointers
  *   workspace: at least moe_mx_workspace_size(M, ...) bytes, 16-byte aligned
  * H and I must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise).
- * info->variant reads MOE_VARIANT_TILED_MXFP8.
+ * info->variant reads MOE_VARIANT_STREAM_MXFP8 or MOE_VARIANT_TILED_MXFP8.
  */
 int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
                       const moe_mx_weights* w, int M, int E, int top_k, int H, int I,

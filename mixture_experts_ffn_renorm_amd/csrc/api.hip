@@ -436,9 +436,11 @@ struct MxLayout {
   size_t qx, sx, qact, sact, total;
 };
 
+// the tile table's block size, with the per-pair case on the streaming
+// kernels (block_m 16)
 int mx_block_m(int M, int E, int top_k) {
   const int B = moe_pick_block_m(M, E, top_k);
-  return B < 64 ? 64 : B;
+  return B < 16 ? 16 : B;
 }
 
 MxLayout mx_layout(int M, int E, int top_k, int H, int I, int B) {
@@ -478,7 +480,7 @@ int moe_mx_quantize(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_
 size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I) {
   if (check_sizes(M_max, E, top_k, H, I) != MOE_OK || !mx_sizes_ok(H, I)) return 0;
   size_t best = 0;
-  for (int B : {64, 128, 256}) best = std::max(best, mx_layout(M_max, E, top_k, H, I, B).total);
+  for (int B : {16, 64, 128, 256}) best = std::max(best, mx_layout(M_max, E, top_k, H, I, B).total);
   return std::max<size_t>(best, kAlign);
 }
 
@@ -495,7 +497,7 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
   const int B = mx_block_m(M, E, top_k);
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
   fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 2 + 2 + kGemm2Launches);
-  if (info != nullptr) info->variant = MOE_VARIANT_TILED_MXFP8;
+  if (info != nullptr) info->variant = B == 16 ? MOE_VARIANT_STREAM_MXFP8 : MOE_VARIANT_TILED_MXFP8;
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !out || !w->w13_codes || !w->w13_scales || !w->w2_codes ||
       !w->w2_scales)
@@ -543,7 +545,7 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
   g.w = reinterpret_cast<const uint16_t*>(w->w13_codes);
   g.w_scales = w->w13_scales;
   g.out = act;
-  MOE_TRY_HIP(launch_gemm1_tiled(g, s));
+  MOE_TRY_HIP(B == 16 ? launch_gemm1_stream(g, s) : launch_gemm1_tiled(g, s));
   MOE_TRY_HIP(launch_mx_quantize(act, M * top_k, I, qact, sact, s));
   g.a_src = reinterpret_cast<const uint16_t*>(qact);
   g.a_scales = sact;
@@ -552,7 +554,7 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
   g.topk_weights = wts;
   g.out = out;
   g.partial = reinterpret_cast<float*>(ws + L.partial);
-  MOE_TRY_HIP(launch_gemm2_tiled(g, s));
+  MOE_TRY_HIP(B == 16 ? launch_gemm2_stream(g, s) : launch_gemm2_tiled(g, s));
   return MOE_OK;
 }
 

@@ -28,6 +28,15 @@
 // pair rows as B), and add their partial tiles through LDS at the end.
 // Pads (id >= M*top_k), features past the end and the K tail copy a zeroed
 // page.
+//
+// MXFP8 operands (kMX; E4M3 bytes, one E8M0 scale per 32 k): the same row
+// slices hold twice the k values, and a wave's two 32-k bf16 steps become
+// one step of the gfx950 scaled MFMA 16x16x128, whose lane (r, g) operand
+// is the two 16-byte chunks g and 4 + g of a 128-k piece -- the chunks the
+// bf16 form reads for its two steps -- with the scale of k block g of its
+// row.  Each slice also copies the rows' scale bytes for its k range into
+// a small LDS area (4-byte copies, one per lane of every wave; rows past
+// the tile and blocks past K read the zeroed page).
 #include <algorithm>
 
 #include "moe_common.h"
@@ -48,14 +57,38 @@ constexpr int kRingBytes = kStages * kStageBytes;          // 72 KB
 constexpr int kWCopies = kWRows / 2 / kWaves;              // 1 KB copies per wave: weights (4)
 constexpr int kXCopies = kBM / 2 / kWaves;                 //                       pair rows (2)
 constexpr int kCopies = kWCopies + kXCopies;
+// MX: 16 scale bytes per row per slice (512 k), 48 rows, copied 4 bytes per
+// lane by all four waves (1 KB of LDS per stage)
+constexpr int kScaleBytes = kWaves * 64 * 4;
+template <bool kMX>
+constexpr int stage_bytes() { return kStageBytes + (kMX ? kScaleBytes : 0); }
 // the waves' partial tiles fit in one ring slot
 static_assert(kWaves * 2 * 64 * 16 <= kStageBytes, "ring slot");
 
 __device__ __forceinline__ int slot(int row, int chunk) { return chunk ^ (row & 15); }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 cat_u32x4(u32x4 lo, u32x4 hi) {
+  const u32x4 l = lo, h = hi;   // by value
+  return i32x8{(int)l[0], (int)l[1], (int)l[2], (int)l[3], (int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+}
+
+// D = A B + C over 128 k of E4M3 operands, each lane's 32 values scaled by
+// 2^(its E8M0 byte - 127).
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ void copy_lds4(const void* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 4, 0, 0);
+}
+
 struct StreamParams {
-  const uint16_t* a_src;      // GEMM 1: x [M, H]; GEMM 2: act [P, I]
+  const uint16_t* a_src;      // GEMM 1: x [M, H]; GEMM 2: act [P, I]  (MX: E4M3 bytes)
   const uint16_t* w;          // GEMM 1: w13 [E, 2I, H]; GEMM 2: w2 [E, H, I]
+  const uint8_t* a_scales;    // MX: E8M0 per 32 k of each a_src row
+  const uint8_t* w_scales;    // MX: E8M0 per 32 k of each weight row
   const int32_t* sorted;
   const int32_t* expert_ids;
   const int32_t* boff;
@@ -65,12 +98,15 @@ struct StreamParams {
   float* partial;             // GEMM 2: [P, H] fp32 weighted partial rows
 };
 
+template <bool kMX>
 __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_kernel(StreamParams prm) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ int s_pair[kBM];
+  constexpr int kSB = stage_bytes<kMX>();
 
   const int P = prm.M * prm.top_k;
-  const int K = prm.H;
+  const int K = kMX ? prm.H / 2 : prm.H;   // row length in 2-byte units (MX: H % 128 == 0)
+  const int nb = prm.H / 32;               // MX: scale bytes per row
   const int ntn = ceil_div(prm.I, 16);
   const int ntiles = prm.boff[prm.E] * ntn;
   const int nslice = ceil_div(K, kKS);
@@ -106,10 +142,24 @@ __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_kernel(StreamParams 
       const int R = 2 * (wv * kXCopies + i) + half;
       xchunk[i] = cl ^ (R & 15);
       const int p = s_pair[R];
-      xsrc[i] = p < P ? prm.a_src + (size_t)(p / prm.top_k) * prm.H : nullptr;
+      xsrc[i] = p < P ? prm.a_src + (size_t)(p / prm.top_k) * K : nullptr;
+    }
+    // MX: lane q = 64 wv + lane copies dword q % 4 of row q / 4's 16 scale
+    // bytes of a slice (rows: 32 weight rows, 16 pair rows, then none)
+    const uint8_t* ssrc = nullptr;
+    const int sq = wv * 64 + lane, srow = sq >> 2, sdw = sq & 3;
+    if constexpr (kMX) {
+      if (srow < kWRows) {
+        const int f = nt * 16 + (srow & 15);
+        if (f < prm.I)
+          ssrc = prm.w_scales + ((size_t)e * 2 * prm.I + (srow < 16 ? f : prm.I + f)) * nb;
+      } else if (srow < kWRows + kBM) {
+        const int p = s_pair[srow - kWRows];
+        if (p < P) ssrc = prm.a_scales + (size_t)(p / prm.top_k) * nb;
+      }
     }
     auto issue = [&](int sl, int buf) {
-      uint8_t* sb = ring + buf * kStageBytes;
+      uint8_t* sb = ring + buf * kSB;
 #pragma unroll
       for (int i = 0; i < kWCopies; ++i) {
         const int k = sl * kKS + wchunk[i] * 8;
@@ -124,16 +174,42 @@ __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_kernel(StreamParams 
         load_lds16(ok ? (const void*)(xsrc[i] + k) : (const void*)kZeroPage,
                    sb + (kWRows + (wv * kXCopies + i) * 2) * kRowB);
       }
+      if constexpr (kMX) {
+        const int blk = sl * 16 + sdw * 4;        // first of this dword's 4 blocks
+        const bool ok = ssrc != nullptr && blk < nb;
+        copy_lds4(ok ? (const void*)(ssrc + blk) : (const void*)kZeroPage,
+                  sb + kStageBytes + wv * 256);
+      }
     };
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     issue(0, 0);
     if (nslice > 1) issue(1, 1);
     for (int sl = 0; sl < nslice; ++sl) {
-      if (sl + 1 < nslice) wait_vmem<kCopies>(); else wait_vmem<0>();
+      if (sl + 1 < nslice) wait_vmem<kCopies + (kMX ? 1 : 0)>(); else wait_vmem<0>();
       barrier_nofence();    // slice sl is in LDS; slice sl-1 has been consumed
       if (sl + 2 < nslice) issue(sl + 2, (sl + 2) % kStages);
-      const uint8_t* sb = ring + (sl % kStages) * kStageBytes;
+      const uint8_t* sb = ring + (sl % kStages) * kSB;
+      if constexpr (kMX) {
+        // chunks 8 wv + kg and 8 wv + 4 + kg: k block 4 wv + kg of the slice
+        const int c0 = wv * 8 + kg, c1 = c0 + 4;
+        const uint8_t* sc = sb + kStageBytes;
+        const i32x8 a0 = cat_u32x4(
+            *reinterpret_cast<const u32x4*>(sb + r16 * kRowB + (slot(r16, c0) << 4)),
+            *reinterpret_cast<const u32x4*>(sb + r16 * kRowB + (slot(r16, c1) << 4)));
+        const i32x8 a1 = cat_u32x4(
+            *reinterpret_cast<const u32x4*>(sb + (16 + r16) * kRowB + (slot(16 + r16, c0) << 4)),
+            *reinterpret_cast<const u32x4*>(sb + (16 + r16) * kRowB + (slot(16 + r16, c1) << 4)));
+        const i32x8 bx = cat_u32x4(
+            *reinterpret_cast<const u32x4*>(sb + (kWRows + r16) * kRowB + (slot(r16, c0) << 4)),
+            *reinterpret_cast<const u32x4*>(sb + (kWRows + r16) * kRowB + (slot(r16, c1) << 4)));
+        const int blk = wv * 4 + kg;
+        const int s0 = sc[r16 * 16 + blk], s1 = sc[(16 + r16) * 16 + blk];
+        const int sx = sc[(kWRows + r16) * 16 + blk];
+        acc0 = mfma_mx(a0, bx, acc0, s0, sx);
+        acc1 = mfma_mx(a1, bx, acc1, s1, sx);
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c = (wv * 2 + j) * 4 + kg;          // 16-byte chunk of the k step
@@ -148,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_kernel(StreamParams 
     }
     // The waves' partial tiles meet in the ring slot two slices behind the last
     // one: every wave has finished reading it (barrier of the last slice).
-    f32x4(*red)[2][64] = reinterpret_cast<f32x4(*)[2][64]>(ring + (nslice % kStages) * kStageBytes);
+    f32x4(*red)[2][64] = reinterpret_cast<f32x4(*)[2][64]>(ring + (nslice % kStages) * kSB);
     red[wv][0][lane] = acc0;
     red[wv][1][lane] = acc1;
     __syncthreads();
@@ -208,17 +284,25 @@ constexpr int kRingBytes = kStages * kStageBytes;            // 60 KB
 constexpr int kWCopies = kWRows / 4 / kWaves;               // 1 KB = 4 rows; per wave (4)
 constexpr int kXCopies = kBM / 4 / kWaves;                  // (1)
 constexpr int kCopies = kWCopies + kXCopies;
+// MX: 8 scale bytes per row per slice (256 k), 80 rows, copied 4 bytes per
+// lane by all four waves (1 KB of LDS per stage)
+constexpr int kScaleBytes = kWaves * 64 * 4;
+template <bool kMX>
+constexpr int stage_bytes() { return kStageBytes + (kMX ? kScaleBytes : 0); }
 
 __device__ __forceinline__ int slot(int row, int chunk) { return chunk ^ (row & 15); }
 
+template <bool kMX>
 __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams prm) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ int s_pair[kBM];
   __shared__ float s_wt[kBM];
   __shared__ int s_e;
+  constexpr int kSB = stage_bytes<kMX>();
 
   const int P = prm.M * prm.top_k;
-  const int H = prm.H, K = prm.I;
+  const int H = prm.H, K = kMX ? prm.I / 2 : prm.I;   // 2-byte units (MX: I % 128 == 0)
+  const int nb = prm.I / 32;                         // MX: scale bytes per row
   const int ntn = ceil_div(H, kWRows);
   const int ntiles = prm.boff[prm.E] * ntn;
   const int ns = ceil_div(K, kKS);
@@ -254,10 +338,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
     const int xchunk = cl ^ (xr & 15);
     const int nt0 = t - b * ntn;
     const int G = (run_end - t) * ns;                 // slices of this run
+    // MX: lane q = 64 wv + lane copies dword q % 2 of row q / 2's 8 scale
+    // bytes of a slice (rows: 64 weight rows, 16 pair rows, then none)
+    const int sq = wv * 64 + lane, srow = sq >> 1, sdw = sq & 1;
+    const uint8_t* sx_src = nullptr;
+    if constexpr (kMX) {
+      if (srow >= kWRows && srow < kWRows + kBM) {
+        const int p = s_pair[srow - kWRows];
+        if (p < P) sx_src = prm.a_scales + (size_t)p * nb;
+      }
+    }
 
     auto issue = [&](int g) {
       const int nt = nt0 + g / ns, sl = g - (g / ns) * ns;
-      uint8_t* sb = ring + (g % kStages) * kStageBytes;
+      uint8_t* sb = ring + (g % kStages) * kSB;
 #pragma unroll
       for (int i = 0; i < kWCopies; ++i) {
         const int R = (wv * kWCopies + i) * 4 + crow;
@@ -270,16 +364,45 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
       const int k = sl * kKS + xchunk * 8;
       load_lds16((xsrc != nullptr && k < K) ? (const void*)(xsrc + k) : (const void*)kZeroPage,
                  sb + (kWRows + wv * 4) * kRowB);
+      if constexpr (kMX) {
+        const int blk = sl * 8 + sdw * 4;          // first of this dword's 4 blocks
+        const uint8_t* src = nullptr;
+        if (srow < kWRows) {
+          const int h = nt * kWRows + srow;
+          if (h < H) src = prm.w_scales + ((size_t)e * H + h) * nb;
+        } else {
+          src = sx_src;
+        }
+        const bool ok = src != nullptr && blk < nb;
+        copy_lds4(ok ? (const void*)(src + blk) : (const void*)kZeroPage, sb + kStageBytes + wv * 256);
+      }
     };
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     issue(0);
     if (G > 1) issue(1);
     for (int g = 0; g < G; ++g) {
-      if (g + 1 < G) wait_vmem<kCopies>(); else wait_vmem<0>();
+      if (g + 1 < G) wait_vmem<kCopies + (kMX ? 1 : 0)>(); else wait_vmem<0>();
       barrier_nofence();    // slice g is in LDS; slice g-1 has been consumed
       if (g + 2 < G) issue(g + 2);
-      const uint8_t* sb = ring + (g % kStages) * kStageBytes;
+      const uint8_t* sb = ring + (g % kStages) * kSB;
+      if constexpr (kMX) {
+        // two 128-k steps per slice: chunks 8 s + kg and 8 s + 4 + kg, block 4 s + kg
+        const uint8_t* sc = sb + kStageBytes;
+        const int Ra = wv * 16 + r16;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int c0 = st * 8 + kg, c1 = c0 + 4;
+          const i32x8 a = cat_u32x4(
+              *reinterpret_cast<const u32x4*>(sb + Ra * kRowB + (slot(Ra, c0) << 4)),
+              *reinterpret_cast<const u32x4*>(sb + Ra * kRowB + (slot(Ra, c1) << 4)));
+          const i32x8 bx = cat_u32x4(
+              *reinterpret_cast<const u32x4*>(sb + (kWRows + r16) * kRowB + (slot(r16, c0) << 4)),
+              *reinterpret_cast<const u32x4*>(sb + (kWRows + r16) * kRowB + (slot(r16, c1) << 4)));
+          const int blk = st * 4 + kg;
+          acc = mfma_mx(a, bx, acc, sc[Ra * 8 + blk], sc[(kWRows + r16) * 8 + blk]);
+        }
+      } else {
 #pragma unroll
       for (int j = 0; j < kKS / 32; ++j) {
         const int c = j * 4 + kg;
@@ -288,6 +411,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
         const u32x4 bx =
             *reinterpret_cast<const u32x4*>(sb + (kWRows + r16) * kRowB + (slot(r16, c) << 4));
         acc = mfma_16x16x32(a, bx, acc);
+      }
       }
       if (g % ns != ns - 1) continue;
 
@@ -327,10 +451,13 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float* __re
 
 }  // namespace ring2
 
+template <bool kMX>
 hipError_t launch_gemm1(const moe_host::GemmArgs& a, hipStream_t s) {
   StreamParams prm{};
   prm.a_src = a.a_src;
   prm.w = a.w;
+  prm.a_scales = a.a_scales;
+  prm.w_scales = a.w_scales;
   prm.sorted = a.sorted_token_ids;
   prm.expert_ids = a.expert_ids;
   prm.boff = a.expert_block_offsets;
@@ -344,27 +471,25 @@ hipError_t launch_gemm1(const moe_host::GemmArgs& a, hipStream_t s) {
   const long long tiles = (long long)a.max_blocks * ((a.I + 15) / 16);
   long long grid = std::min<long long>(tiles, 2LL * moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
+  constexpr int kRing = kStages * stage_bytes<kMX>();
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm1_stream_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRingBytes);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm1_stream_kernel<kMX>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRing);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL(gemm1_stream_kernel, dim3((unsigned)grid), dim3(kThreads), kRingBytes, s, prm);
+  hipLaunchKernelGGL(gemm1_stream_kernel<kMX>, dim3((unsigned)grid), dim3(kThreads), kRing, s, prm);
   return hipGetLastError();
 }
 
-}  // namespace
-
-namespace moe_host {
-
-hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s) { return launch_gemm1(a, s); }
-
-hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s) {
+template <bool kMX>
+hipError_t launch_gemm2(const moe_host::GemmArgs& a, hipStream_t s) {
   StreamParams prm{};
   prm.a_src = a.a_src;
   prm.w = a.w;
+  prm.a_scales = a.a_scales;
+  prm.w_scales = a.w_scales;
   prm.sorted = a.sorted_token_ids;
   prm.expert_ids = a.expert_ids;
   prm.boff = a.expert_block_offsets;
@@ -377,21 +502,33 @@ hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s) {
   prm.out = a.out;
   prm.partial = a.partial;
   const long long tiles = (long long)a.max_blocks * ((a.H + ring2::kWRows - 1) / ring2::kWRows);
-  long long grid = std::min<long long>(tiles, 2LL * device_cu_count());
+  long long grid = std::min<long long>(tiles, 2LL * moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
+  constexpr int kRing = ring2::kStages * ring2::stage_bytes<kMX>();
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&ring2::gemm2_ring_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         ring2::kRingBytes);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&ring2::gemm2_ring_kernel<kMX>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRing);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL(ring2::gemm2_ring_kernel, dim3((unsigned)grid), dim3(ring2::kThreads),
-                     ring2::kRingBytes, s, prm);
+  hipLaunchKernelGGL(ring2::gemm2_ring_kernel<kMX>, dim3((unsigned)grid), dim3(ring2::kThreads),
+                     kRing, s, prm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
+  return moe_host::launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
+}
+
+}  // namespace
+
+namespace moe_host {
+
+hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s) {
+  return a.mx ? launch_gemm1<true>(a, s) : launch_gemm1<false>(a, s);
+}
+
+hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s) {
+  return a.mx ? launch_gemm2<true>(a, s) : launch_gemm2<false>(a, s);
 }
 
 hipError_t launch_combine_partials(const float* partial, int M, int top_k, int H, uint16_t* out,

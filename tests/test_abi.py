@@ -198,8 +198,8 @@ def test_forward_mxfp8_argument_checks(H, I, M, status):
                                NULL, NULL, 0, ctypes.byref(info), NULL)
     assert st == status
     if status == 0:
-        assert info.variant == moe.MOE_VARIANT_TILED_MXFP8 and info.launches == 0
-        assert info.block_m == 64
+        assert info.variant == moe.MOE_VARIANT_STREAM_MXFP8 and info.launches == 0
+        assert info.block_m == 16
 
 
 def test_mx_workspace_and_quantize_checks():

@@ -8,10 +8,12 @@ oracle's mx_quantize and forward_mxfp8.
   neighbours, blocks that saturate at 448.
 * The layer: routing ids where the top-k margin exceeds 1e-4, weights to
   1e-5, outputs within 2e-2 max-abs (relative to max |ref|) and 5e-3
-  mean-relative, on a small ragged layer, the Qwen3-30B-A3B decode shape
-  (64 tokens), the Qwen1.5-MoE shape (I = 1408 = 11 * 128) and the Qwen3
-  prefill shape with its Zipf prior (block_m 256), plus a poisoned
-  workspace.
+  mean-relative, through the weight-streaming kernels (block_m 16: small
+  layers, the Qwen3-30B-A3B decode shape at 1, 8 and 64 tokens, the
+  Qwen1.5-MoE shape whose I = 1408 leaves a ragged last slice, 256 experts)
+  and the tiled kernels (a mid layer, the Qwen1.5-MoE shape at 512 tokens,
+  the Qwen3 prefill shape with its Zipf prior at block_m 256), plus a
+  poisoned workspace.
 """
 
 from __future__ import annotations
@@ -92,8 +94,9 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
     print(f"mxfp8 case {lay['name']} M={lay['M']} E={lay['E']} k={lay['top_k']} "
           f"H={lay['H']} I={lay['I']}", flush=True)
     out, ids, wts, info = run_mx(lay, **kw)
-    assert info["variant"] == moe.MOE_VARIANT_TILED_MXFP8
-    assert info["block_m"] == max(64, moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"]))
+    B = max(16, moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"]))
+    assert info["block_m"] == B
+    assert info["variant"] == (moe.MOE_VARIANT_STREAM_MXFP8 if B == 16 else moe.MOE_VARIANT_TILED_MXFP8)
     toks = h.sample_tokens(lay["M"], n_tokens, seed)
     ref = mo.forward_mxfp8(lay, tokens=toks)
     r = ref["route"]
@@ -106,9 +109,16 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
     return out
 
 
+# block_m 16 (streaming): toy M=5, Qwen3 decode M=1, 8 and 64, Qwen1.5 M=16
+# (I = 1408: a ragged last slice in both streaming kernels), 256 experts
+# M=8; tiled: toy M=70, Qwen1.5 M=512, Qwen3 prefill (block_m 256)
 MX_CASES = [("toy", 5, dict(E=8, top_k=2, H=256, I=128)),
             ("toy", 70, dict(E=6, top_k=2, H=384, I=256)),
+            ("qwen3_decode", 1, {}),
+            ("qwen3_decode", 8, {}),
             ("qwen3_decode", 64, {}),
+            ("qwen15", 16, {}),
+            ("wide256", 8, {}),
             ("qwen15", 512, {}),
             ("qwen3_prefill", 4096, {})]
 
