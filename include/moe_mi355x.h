@@ -94,7 +94,9 @@ const char* moe_strerror(int status);
 /* The block size (block_m) moe_forward uses for a batch of M tokens: the
  * compiled tile table.  Returns 1 (per-pair GEMVs) when M >= 1 and
  * M*top_k*4 <= E; otherwise, keyed on the mean number of pairs per expert
- * (M*top_k/E), 16 (weight-streaming kernels), 64, 128 or 256 (tiled). */
+ * (M*top_k/E): 16 (weight-streaming kernels) up to 8 pairs per expert, then
+ * the tiled kernels: 64 up to 48, 128 below 128, 256 below 192, 128 from 192
+ * on (measured per shape). */
 int moe_pick_block_m(int M, int E, int top_k);
 
 /*
@@ -312,8 +314,9 @@ size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I);
  * accumulation) with SiLU(gate)*up, act stored bf16; act quantized to
  * MXFP8; GEMM 2 likewise into bf16 pair-order rows; the weighted top-k sum
  * per token.  Index lists with block_m = moe_pick_block_m(M, E, top_k), at
- * least 16: weight-streaming kernels at block_m 16 (small batches, also the
- * per-pair case), tiled kernels above.
+ * least 16, and 256 from 128 pairs per expert on: weight-streaming kernels
+ * at block_m 16 (small batches, also the per-pair case), tiled kernels
+ * above.
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, info,
  *   stream: as for moe_forward;  w: host struct of device pointers

@@ -215,8 +215,13 @@ int moe_pick_block_m(int M, int E, int top_k) {
   const double per_expert = (double)M * top_k / E;
   if (per_expert <= 8.0) return 16;
   if (per_expert <= 48.0) return 64;
+  // Measured on the copy-wave tiles: 128-pair blocks up to 128 pairs per
+  // expert; 256 where a 128-pair expert would end in a second, nearly empty
+  // block that streams its weights again (Qwen1.5 shape, 136 per expert);
+  // 128 again from 192 on, where 256-pair blocks leave more pad quarters.
   if (per_expert < 128.0) return 128;
-  return 256;
+  if (per_expert < 192.0) return 256;
+  return 128;
 }
 
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bias, int M,
@@ -440,7 +445,10 @@ struct MxLayout {
 // kernels (block_m 16)
 int mx_block_m(int M, int E, int top_k) {
   const int B = moe_pick_block_m(M, E, top_k);
-  return B < 16 ? 16 : B;
+  if (B < 16) return 16;
+  // MXFP8 tiles have no copy-wave form; 256-pair tiles suit them from 128
+  // pairs per expert on
+  return (double)M * top_k / E >= 128.0 ? 256 : B;
 }
 
 MxLayout mx_layout(int M, int E, int top_k, int H, int I, int B) {

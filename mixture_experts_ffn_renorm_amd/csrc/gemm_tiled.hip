@@ -25,6 +25,16 @@
 // about 1.3x the rate).  Quarters of the block that hold only pads (the
 // tail of an expert's last block) skip their MFMAs.
 //
+// Copy waves (bf16 tiles): each workgroup has four more waves, one per
+// SIMD, that issue every global-to-LDS copy and do no MFMA work, and the
+// eight MFMA waves issue no copies.  The per-CU copy path drains a 64 KB
+// stage far slower than waves can issue it, so a copy instruction blocks
+// its wave at issue; with the copies in their own waves that block never
+// holds up an MFMA (the MFMA waves spent a third of their time there).
+// Copy and MFMA waves run separate loops over the same barriers, so
+// neither keeps the other's registers live (104 VGPRs at 128 pairs, 168 at
+// 256, for 12 waves a CU).  MXFP8 tiles keep the eight-wave form.
+//
 // Persistent workgroups, one per CU.  Each XCD owns a contiguous range of
 // tiles (block-major, all column tiles of a block side by side) and its
 // workgroups take them round robin, so the column tiles of one block (same
@@ -70,15 +80,20 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRowBytes = kBK * 2;
 constexpr int kMeta = 5;         // tile metadata buffers (pair ids, expert)
 
-// Tile shape per block size BM: 256 weight rows x BM pairs, waves in a
-// 4 (features, 64 rows each) x 2 (pair halves) layout.
-template <int BM, bool kMX = false>
+// Tile shape per block size BM: 256 weight rows x BM pairs, MFMA waves in a
+// 4 (features, 64 rows each) x 2 (pair halves) layout.  With kPC four more
+// waves (one per SIMD) issue every copy and the eight MFMA waves issue
+// none, so a copy that blocks at issue never holds up an MFMA.
+template <int BM, bool kMX = false, bool kPC = false>
 struct TileCfg {
+  static_assert(!(kMX && kPC), "copy waves: bf16 operands only");
   static constexpr int kBN = 256;                      // weight rows per tile
   static constexpr int kWF = kBN / 64;
   static constexpr int kWP = kWaves / kWF;
-  static constexpr int kWGroups = kBN / 8 / kWaves;   // 8-row W groups per wave (2 or 4)
-  static constexpr int kXGroups = BM / 8 / kWaves;    // 8-row X groups per wave (1, 2 or 4)
+  static constexpr int kCopyWaves = kPC ? 4 : kWaves;  // waves that issue copies
+  static constexpr int kThreadsT = (kWaves + (kPC ? 4 : 0)) * 64;
+  static constexpr int kWGroups = kBN / 8 / kCopyWaves;   // 8-row W groups per copy wave
+  static constexpr int kXGroups = BM / 8 / kCopyWaves;    // 8-row X groups per copy wave
   // copy instructions per stage (MX: one more, the scales)
   static constexpr int kLoads = kWGroups + kXGroups + (kMX ? 1 : 0);
   static constexpr int kOperandBytes = (kBN + BM) * kRowBytes;       // 40, 48 or 64 KB
@@ -127,9 +142,10 @@ struct TileParams {
   uint16_t* out;           // GEMM 1: act [P, I]; GEMM 2: pair-order product [P, H]
 };
 
-template <int BM, bool kGemm1, bool kMX>
-__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParams prm) {
-  using C = TileCfg<BM, kMX>;
+template <int BM, bool kGemm1, bool kMX, bool kPC = false>
+__global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_tiled_kernel(
+    const TileParams prm) {
+  using C = TileCfg<BM, kMX, kPC>;
   constexpr int NT = C::kNT;
   constexpr int kStages = C::kStages;
   constexpr int kBN = C::kBN;
@@ -154,14 +170,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   const int G = nmine * nk;  // stages of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lrow = lane >> 3, lpos = lane & 7;
+  // copy wave index (kPC: waves kWaves.. copy, waves 0..kWaves-1 multiply)
+  const bool copier = !kPC || wv >= kWaves;
+  const bool mfma_wave = !kPC || wv < kWaves;
+  const int cw = kPC ? wv - kWaves : wv;
 
   // ---- metadata copies of tile i into buffer i % kMeta ----
   auto issue_meta = [&](int i) {
     if (i >= nmine) return;
     const int b = (j0 + i * nslots) / ntn;
-    if (wv == 0 && lane < BM / 4)
+    if (copier && cw == 0 && lane < BM / 4)
       load_lds16(prm.sorted + (size_t)b * BM + 4 * lane, reinterpret_cast<uint8_t*>(s_pair[i % kMeta]));
-    if (wv == 1 && lane == 0) load_lds4(prm.expert_ids + b, &s_exp[i % kMeta]);
+    if (copier && cw == 1 && lane == 0) load_lds4(prm.expert_ids + b, &s_exp[i % kMeta]);
   };
 
   // ---- per-lane copy sources of the tile being issued ----
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     const int e = s_exp[buf];
 #pragma unroll
     for (int gi = 0; gi < C::kWGroups; ++gi) {
-      const int R = (wv + kWaves * gi) * 8 + lrow;
+      const int R = (cw + C::kCopyWaves * gi) * 8 + lrow;
       const uint16_t* row = nullptr;
       if (kGemm1) {
         const int f = nt * kHalf + (R % kHalf);
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     }
 #pragma unroll
     for (int gi = 0; gi < C::kXGroups; ++gi) {
-      const int R = (wv + kWaves * gi) * 8 + lrow;
+      const int R = (cw + C::kCopyWaves * gi) * 8 + lrow;
       const int p = s_pair[buf][R];
       const uint16_t* row = nullptr;
       if (p < P)
@@ -247,15 +267,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
 #pragma unroll
     for (int gi = 0; gi < C::kWGroups; ++gi) {
       const uint16_t* src = wsrc[gi];
-      if (tail && (lpos ^ swz((wv + kWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
-      load_lds16(src, sb + (wv + kWaves * gi) * 8 * kRowBytes);
+      if (tail && (lpos ^ swz((cw + C::kCopyWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
+      load_lds16(src, sb + (cw + C::kCopyWaves * gi) * 8 * kRowBytes);
       wsrc[gi] += wstep[gi];
     }
 #pragma unroll
     for (int gi = 0; gi < C::kXGroups; ++gi) {
       const uint16_t* src = xsrc[gi];
-      if (tail && (lpos ^ swz((wv + kWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
-      load_lds16(src, sb + (kBN + (wv + kWaves * gi) * 8) * kRowBytes);
+      if (tail && (lpos ^ swz((cw + C::kCopyWaves * gi) * 8 + lrow)) * 8 >= kend) src = zero;
+      load_lds16(src, sb + (kBN + (cw + C::kCopyWaves * gi) * 8) * kRowBytes);
       xsrc[gi] += xstep[gi];
     }
     if constexpr (kMX) {
@@ -276,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   // only on r16 and each tile's offset is a constant added to one base per
   // operand and k half.
   constexpr int QS = BM / 4, TQ = NT / 2;   // pairs and B tiles per quarter
-  const int wf = wv % C::kWF, wp = wv / C::kWF;
+  const int wf = wv % C::kWF, wp = (wv / C::kWF) % C::kWP;
   const int r16 = lane & 15, kg = lane >> 4;
   auto brow = [&](int j) { return (j < TQ ? wp : wp + 2) * QS + 16 * (j % TQ); };
   const int arow0 = kGemm1 ? wf * 32 : wf * 64;
@@ -302,9 +322,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
   issue_meta(1);
   wait_vmem<0>();
   __syncthreads();
-#pragma unroll
-  for (int g = 0; g < kStages - 1; ++g)
-    if (g < G) issue_stage();
 
   bool act0 = true, act1 = true;   // this wave's quarters hold a pair
   // MX: one scaled MFMA per (A tile, B tile) per stage; the lane's operand
@@ -347,26 +364,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         if (!(q == 0 ? act0 : act1)) continue;
-        u32x4 bfr[TQ];
+        // B tiles in groups of JB (copy-wave kernels: fewer live registers)
+        constexpr int JB = (kPC && TQ > 2) ? TQ / 2 : TQ;
 #pragma unroll
-        for (int j = 0; j < TQ; ++j)
-          bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] +
-                                                   (q * 2 * QS + 16 * j) * kRowBytes);
+        for (int j0 = 0; j0 < TQ; j0 += JB) {
+          u32x4 bfr[JB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < JB; ++j)
+            bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] +
+                                                     (q * 2 * QS + 16 * (j0 + j)) * kRowBytes);
 #pragma unroll
-          for (int j = 0; j < TQ; ++j)
-            acc[i][q * TQ + j] = mfma_16x16x32(af[i], bfr[j], acc[i][q * TQ + j]);
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < JB; ++j)
+              acc[i][q * TQ + j0 + j] = mfma_16x16x32(af[i], bfr[j], acc[i][q * TQ + j0 + j]);
+        }
       }
     }
   };
+  // Consumption of stage g by an MFMA wave (after the stage's barrier):
+  // MFMAs, and the tile epilogue after the tile's last k step.
   int c_i = 0, c_kt = 0, c_buf = 0, c_slot = 0;
-  for (int g = 0; g < G; ++g) {
-    // stage g has landed once at most the later stages' copies are pending
-    if (kStages == 3 && g + 1 < G) wait_vmem<C::kLoads>(); else wait_vmem<0>();
-    // Every wave's part of stage g is in LDS, and stage g-1 is consumed.
-    barrier_nofence();
-    if (g + kStages - 1 < G) issue_stage();
+  auto consume = [&]() {
     const int i_tile = c_i, kt = c_kt;
     const int buf = c_buf;
     if (kt == 0) {
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
     }
     c_slot = c_slot == kStages - 1 ? 0 : c_slot + 1;
     if (++c_kt == nk) { c_kt = 0; ++c_i; c_buf = c_buf == kMeta - 1 ? 0 : c_buf + 1; }
-    if (kt != nk - 1) continue;
+    if (kt != nk - 1) return;
 
     // ---- tile epilogue: lane holds features 4*kg + q of each A tile, pair r16 of each B tile ----
     const int jt = j0 + i_tile * nslots;
@@ -419,6 +438,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const TileParam
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+
+  if constexpr (kPC) {
+    // Copy waves and MFMA waves run separate loops with the same barriers,
+    // so neither keeps the other's registers live.
+    if (copier) {
+#pragma unroll
+      for (int g = 0; g < kStages - 1; ++g)
+        if (g < G) issue_stage();
+      for (int g = 0; g < G; ++g) {
+        // stage g has landed once at most the later stages' copies are pending
+        if (kStages == 3 && g + 1 < G) wait_vmem<C::kLoads>(); else wait_vmem<0>();
+        barrier_nofence();   // stage g is in LDS; stage g-1 has been consumed
+        if (g + kStages - 1 < G) issue_stage();
+      }
+    } else {
+      for (int g = 0; g < G; ++g) {
+        barrier_nofence();
+        consume();
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kStages - 1; ++g)
+      if (g < G) issue_stage();
+    for (int g = 0; g < G; ++g) {
+      // stage g has landed once at most the later stages' copies are pending
+      if (kStages == 3 && g + 1 < G) wait_vmem<C::kLoads>(); else wait_vmem<0>();
+      // Every wave's part of stage g is in LDS, and stage g-1 is consumed.
+      barrier_nofence();
+      if (g + kStages - 1 < G) issue_stage();
+      consume();
+    }
   }
 }
 
@@ -453,9 +505,10 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __res
   *reinterpret_cast<u32x4*>(out + (size_t)t * H + h) = o;
 }
 
-template <int BM, bool kGemm1, bool kMX = false>
+template <int BM, bool kGemm1, bool kMX = false, bool kPC = false>
 hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* out) {
-  constexpr int kBN = TileCfg<BM, kMX>::kBN;
+  using C = TileCfg<BM, kMX, kPC>;
+  constexpr int kBN = C::kBN;
   TileParams prm;
   prm.a_src = a.a_src;
   prm.w = a.w;
@@ -475,17 +528,17 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* ou
   const long long tiles = (long long)a.max_blocks * prm.ntn;
   long long grid = std::min<long long>(tiles, moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
-  const size_t lds = TileCfg<BM, kMX>::kRingBytes;
+  const size_t lds = C::kRingBytes;
   static bool attr_set = false;   // idempotent; racing first calls set the same value
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX>),
+        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX, kPC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX>), dim3((unsigned)grid), dim3(kThreads), lds, s,
-                     prm);
+  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX, kPC>), dim3((unsigned)grid), dim3(C::kThreadsT),
+                     lds, s, prm);
   return hipGetLastError();
 }
 
@@ -499,9 +552,9 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s) {
     if (a.block_m == 128) return launch_tiled<128, true, true>(a, s, a.out);
     return launch_tiled<64, true, true>(a, s, a.out);
   }
-  if (a.block_m == 256) return launch_tiled<256, true>(a, s, a.out);
-  if (a.block_m == 128) return launch_tiled<128, true>(a, s, a.out);
-  return launch_tiled<64, true>(a, s, a.out);
+  if (a.block_m == 256) return launch_tiled<256, true, false, true>(a, s, a.out);
+  if (a.block_m == 128) return launch_tiled<128, true, false, true>(a, s, a.out);
+  return launch_tiled<64, true, false, true>(a, s, a.out);
 }
 
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
@@ -512,9 +565,9 @@ hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
           : a.block_m == 128 ? launch_tiled<128, false, true>(a, s, rows)
                              : launch_tiled<64, false, true>(a, s, rows);
   else
-    err = a.block_m == 256   ? launch_tiled<256, false>(a, s, rows)
-          : a.block_m == 128 ? launch_tiled<128, false>(a, s, rows)
-                             : launch_tiled<64, false>(a, s, rows);
+    err = a.block_m == 256   ? launch_tiled<256, false, false, true>(a, s, rows)
+          : a.block_m == 128 ? launch_tiled<128, false, false, true>(a, s, rows)
+                             : launch_tiled<64, false, false, true>(a, s, rows);
   if (err != hipSuccess) return err;
   const long long n8 = (long long)a.M * (a.H / 8);
   hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, rows,

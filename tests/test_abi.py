@@ -59,8 +59,8 @@ def test_tile_table():
     assert moe.moe_pick_block_m(512, 60, 4) == 64
     assert moe.moe_pick_block_m(1024, 60, 4) == 128
     assert moe.moe_pick_block_m(2048, 60, 4) == 256
-    assert moe.moe_pick_block_m(4096, 128, 8) == 256
-    assert moe.moe_pick_block_m(8192, 256, 8) == 256
+    assert moe.moe_pick_block_m(4096, 128, 8) == 128
+    assert moe.moe_pick_block_m(8192, 256, 8) == 128
     assert moe.moe_pick_block_m(8, 256, 8) == 1
     assert moe.moe_pick_block_m(9, 256, 8) == 16
 

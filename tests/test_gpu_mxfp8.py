@@ -95,6 +95,8 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
           f"H={lay['H']} I={lay['I']}", flush=True)
     out, ids, wts, info = run_mx(lay, **kw)
     B = max(16, moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"]))
+    if lay["M"] * lay["top_k"] >= 128 * lay["E"]:
+        B = 256   # the MXFP8 tiles keep 256-pair blocks from 128 pairs per expert on
     assert info["block_m"] == B
     assert info["variant"] == (moe.MOE_VARIANT_STREAM_MXFP8 if B == 16 else moe.MOE_VARIANT_TILED_MXFP8)
     toks = h.sample_tokens(lay["M"], n_tokens, seed)
