@@ -314,9 +314,8 @@ size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I);
  * accumulation) with SiLU(gate)*up, act stored bf16; act quantized to
  * MXFP8; GEMM 2 likewise into bf16 pair-order rows; the weighted top-k sum
  * per token.  Index lists with block_m = moe_pick_block_m(M, E, top_k), at
- * least 16, and 256 from 128 pairs per expert on: weight-streaming kernels
- * at block_m 16 (small batches, also the per-pair case), tiled kernels
- * above.
+ * least 16: weight-streaming kernels at block_m 16 (small batches, also the
+ * per-pair case), tiled kernels above.
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, info,
  *   stream: as for moe_forward;  w: host struct of device pointers

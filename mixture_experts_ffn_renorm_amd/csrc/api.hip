@@ -445,10 +445,7 @@ struct MxLayout {
 // kernels (block_m 16)
 int mx_block_m(int M, int E, int top_k) {
   const int B = moe_pick_block_m(M, E, top_k);
-  if (B < 16) return 16;
-  // MXFP8 tiles have no copy-wave form; 256-pair tiles suit them from 128
-  // pairs per expert on
-  return (double)M * top_k / E >= 128.0 ? 256 : B;
+  return B < 16 ? 16 : B;
 }
 
 MxLayout mx_layout(int M, int E, int top_k, int H, int I, int B) {

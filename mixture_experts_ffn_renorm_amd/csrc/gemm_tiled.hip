@@ -33,7 +33,8 @@
 // holds up an MFMA (the MFMA waves spent a third of their time there).
 // Copy and MFMA waves run separate loops over the same barriers, so
 // neither keeps the other's registers live (104 VGPRs at 128 pairs, 168 at
-// 256, for 12 waves a CU).  MXFP8 tiles keep the eight-wave form.
+// 256, for 12 waves a CU).  MXFP8 tiles take the same form at 128 pairs
+// (each copy wave also copies the scale bytes of two 64-row groups).
 //
 // Persistent workgroups, one per CU.  Each XCD owns a contiguous range of
 // tiles (block-major, all column tiles of a block side by side) and its
@@ -86,7 +87,6 @@ constexpr int kMeta = 5;         // tile metadata buffers (pair ids, expert)
 // none, so a copy that blocks at issue never holds up an MFMA.
 template <int BM, bool kMX = false, bool kPC = false>
 struct TileCfg {
-  static_assert(!(kMX && kPC), "copy waves: bf16 operands only");
   static constexpr int kBN = 256;                      // weight rows per tile
   static constexpr int kWF = kBN / 64;
   static constexpr int kWP = kWaves / kWF;
@@ -95,7 +95,9 @@ struct TileCfg {
   static constexpr int kWGroups = kBN / 8 / kCopyWaves;   // 8-row W groups per copy wave
   static constexpr int kXGroups = BM / 8 / kCopyWaves;    // 8-row X groups per copy wave
   // copy instructions per stage (MX: one more, the scales)
-  static constexpr int kLoads = kWGroups + kXGroups + (kMX ? 1 : 0);
+  // MX: the scale bytes of 512 rows per stage, 64 rows per 4-byte copy
+  static constexpr int kScaleCopies = kMX ? kWaves / kCopyWaves : 0;
+  static constexpr int kLoads = kWGroups + kXGroups + kScaleCopies;
   static constexpr int kOperandBytes = (kBN + BM) * kRowBytes;       // 40, 48 or 64 KB
   static constexpr int kScaleRows = kWaves * 64;                     // MX: 4 bytes each
   static constexpr int kStageBytes = kOperandBytes + (kMX ? kScaleRows * 4 : 0);
@@ -193,10 +195,10 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   int wstep[C::kWGroups], xstep[C::kXGroups];
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroPage);
   const bool k_tail = (K % kBK) != 0;
-  // MX: this lane copies the 4 scale bytes of row 64 wv + lane of the tile
-  // (weight rows, then pair rows, then unused) for each stage
-  const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(kZeroPage);
-  int sstep = 0;
+  // MX: this lane copies the 4 scale bytes of rows 64 (cw + kCopyWaves h) +
+  // lane of the tile (weight rows, then pair rows, then unused) per stage
+  const uint8_t* ssrc[C::kScaleCopies > 0 ? C::kScaleCopies : 1];
+  int sstep[C::kScaleCopies > 0 ? C::kScaleCopies : 1];
 
   // Point the copy sources at tile i (its metadata is in LDS), and start the
   // metadata copies of tile i + 2.
@@ -231,8 +233,9 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       xsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
       xstep[gi] = row != nullptr ? kBK : 0;
     }
-    if constexpr (kMX) {
-      const int R = wv * 64 + lane, nb = Ke / 32;
+#pragma unroll
+    for (int h = 0; h < C::kScaleCopies; ++h) {
+      const int R = (cw + C::kCopyWaves * h) * 64 + lane, nb = Ke / 32;
       const uint8_t* srow = nullptr;
       if (R < kBN) {
         if (kGemm1) {
@@ -248,8 +251,8 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
         if (p < P)
           srow = prm.a_scales + (size_t)(kGemm1 ? p / prm.top_k : p) * nb;
       }
-      ssrc = srow != nullptr ? srow : reinterpret_cast<const uint8_t*>(kZeroPage);
-      sstep = srow != nullptr ? 4 : 0;
+      ssrc[h] = srow != nullptr ? srow : reinterpret_cast<const uint8_t*>(kZeroPage);
+      sstep[h] = srow != nullptr ? 4 : 0;
     }
     issue_meta(i + 2);
   };
@@ -278,9 +281,10 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       load_lds16(src, sb + (kBN + (cw + C::kCopyWaves * gi) * 8) * kRowBytes);
       xsrc[gi] += xstep[gi];
     }
-    if constexpr (kMX) {
-      load_lds4(ssrc, sb + C::kOperandBytes + wv * 256);
-      ssrc += sstep;
+#pragma unroll
+    for (int h = 0; h < C::kScaleCopies; ++h) {
+      load_lds4(ssrc[h], sb + C::kOperandBytes + (cw + C::kCopyWaves * h) * 256);
+      ssrc[h] += sstep[h];
     }
   };
 
@@ -549,7 +553,7 @@ namespace moe_host {
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s) {
   if (a.mx) {
     if (a.block_m == 256) return launch_tiled<256, true, true>(a, s, a.out);
-    if (a.block_m == 128) return launch_tiled<128, true, true>(a, s, a.out);
+    if (a.block_m == 128) return launch_tiled<128, true, true, true>(a, s, a.out);
     return launch_tiled<64, true, true>(a, s, a.out);
   }
   if (a.block_m == 256) return launch_tiled<256, true, false, true>(a, s, a.out);
@@ -562,7 +566,7 @@ hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
   hipError_t err;
   if (a.mx)
     err = a.block_m == 256   ? launch_tiled<256, false, true>(a, s, rows)
-          : a.block_m == 128 ? launch_tiled<128, false, true>(a, s, rows)
+          : a.block_m == 128 ? launch_tiled<128, false, true, true>(a, s, rows)
                              : launch_tiled<64, false, true>(a, s, rows);
   else
     err = a.block_m == 256   ? launch_tiled<256, false, false, true>(a, s, rows)

@@ -12,7 +12,7 @@ oracle's mx_quantize and forward_mxfp8.
   layers, the Qwen3-30B-A3B decode shape at 1, 8 and 64 tokens, the
   Qwen1.5-MoE shape whose I = 1408 leaves a ragged last slice, 256 experts)
   and the tiled kernels (a mid layer, the Qwen1.5-MoE shape at 512 tokens,
-  the Qwen3 prefill shape with its Zipf prior at block_m 256), plus a
+  the Qwen3 prefill shape with its Zipf prior at block_m 128), plus a
   poisoned workspace.
 """
 
@@ -95,8 +95,6 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
           f"H={lay['H']} I={lay['I']}", flush=True)
     out, ids, wts, info = run_mx(lay, **kw)
     B = max(16, moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"]))
-    if lay["M"] * lay["top_k"] >= 128 * lay["E"]:
-        B = 256   # the MXFP8 tiles keep 256-pair blocks from 128 pairs per expert on
     assert info["block_m"] == B
     assert info["variant"] == (moe.MOE_VARIANT_STREAM_MXFP8 if B == 16 else moe.MOE_VARIANT_TILED_MXFP8)
     toks = h.sample_tokens(lay["M"], n_tokens, seed)
@@ -113,9 +111,11 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
 
 # block_m 16 (streaming): toy M=5, Qwen3 decode M=1, 8 and 64, Qwen1.5 M=16
 # (I = 1408: a ragged last slice in both streaming kernels), 256 experts
-# M=8; tiled: toy M=70, Qwen1.5 M=512, Qwen3 prefill (block_m 256)
+# M=8; tiled: toy M=70, Qwen1.5 M=512 (block_m 64), toy M=300 (block_m 128,
+# the copy-wave tiles), Qwen3 prefill (block_m 128)
 MX_CASES = [("toy", 5, dict(E=8, top_k=2, H=256, I=128)),
             ("toy", 70, dict(E=6, top_k=2, H=384, I=256)),
+            ("toy", 300, dict(E=6, top_k=2, H=384, I=256)),
             ("qwen3_decode", 1, {}),
             ("qwen3_decode", 8, {}),
             ("qwen3_decode", 64, {}),
