@@ -413,7 +413,55 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
     for (int j = 0; j < NT; ++j) {
       if (!(j < TQ ? act0 : act1)) continue;
       const int p = s_pair[buf][brow(j) + r16];
-      if (p < P) {
+      // 16-byte stores through a lane-pair exchange (not at 256 copy-wave
+      // pairs, whose 168 registers leave no room)
+      constexpr bool kStore16 = !(kPC && BM == 256);
+      if constexpr (kStore16 && kGemm1) {
+        // GEMM 1: lanes kg and kg ^ 1 swap halves so that the even lane
+        // holds act columns 4 kg .. 4 kg + 7 of gate tile 0 and the odd lane
+        // columns 4 (kg - 1) .. 4 kg + 3 of gate tile 1 (I % 8 == 0).
+        const int I = prm.I;
+        const bool odd = (kg & 1) != 0;
+        u32x2 v[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const f32x4 gt = acc[i][j], up = acc[i + 2][j];
+          v[i][0] = pack_bf16x2(silu_mul(gt[0], up[0]), silu_mul(gt[1], up[1]));
+          v[i][1] = pack_bf16x2(silu_mul(gt[2], up[2]), silu_mul(gt[3], up[3]));
+        }
+        const u32x2 send = odd ? v[0] : v[1];
+        u32x2 recv;
+        recv[0] = __shfl_xor(send[0], 16, kWave);
+        recv[1] = __shfl_xor(send[1], 16, kWave);
+        const u32x4 o = odd ? u32x4{recv[0], recv[1], v[1][0], v[1][1]}
+                            : u32x4{v[0][0], v[0][1], recv[0], recv[1]};
+        const int n = nt * kHalf + wf * 32 + 16 * (odd ? 1 : 0) + 4 * (kg & ~1);
+        if (p < P && n < I) *reinterpret_cast<u32x4*>(prm.out + (size_t)p * I + n) = o;
+      } else if constexpr (kStore16) {
+        // GEMM 2: 16-byte stores.  Lanes kg and kg ^ 1 (same pair) swap
+        // halves so that, for A tiles i and i + 1, the even lane holds
+        // features 4 kg .. 4 kg + 7 of tile i and the odd lane features
+        // 4 (kg - 1) .. 4 kg + 3 of tile i + 1.
+        const int H = prm.H;
+        const bool odd = (kg & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          u32x2 v0, v1;
+          v0[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          v0[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          v1[0] = pack_bf16x2(acc[i + 1][j][0], acc[i + 1][j][1]);
+          v1[1] = pack_bf16x2(acc[i + 1][j][2], acc[i + 1][j][3]);
+          const u32x2 send = odd ? v0 : v1;
+          u32x2 recv;
+          recv[0] = __shfl_xor(send[0], 16, kWave);
+          recv[1] = __shfl_xor(send[1], 16, kWave);
+          const u32x4 o = odd ? u32x4{recv[0], recv[1], v1[0], v1[1]}
+                              : u32x4{v0[0], v0[1], recv[0], recv[1]};
+          // H % 8 == 0 and h % 8 == 0: the 8 features exist or none do
+          const int h = nt * kBN + wf * 64 + 16 * (i + (odd ? 1 : 0)) + 4 * (kg & ~1);
+          if (p < P && h < H) *reinterpret_cast<u32x4*>(prm.out + (size_t)p * H + h) = o;
+        }
+      } else if (p < P) {
         if (kGemm1) {
           const int I = prm.I;
 #pragma unroll
