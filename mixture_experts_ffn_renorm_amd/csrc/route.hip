@@ -141,46 +141,48 @@ __global__ __launch_bounds__(256) void route_logits_gemv_kernel(
 }
 
 // Router logits for large batches: LDS-tiled MFMA GEMM over a tile of BT
-// tokens (32 or 64) x 128 experts, 4 waves (2 expert halves x 2 token
-// halves, each 64 experts x BT/2 tokens).  K goes through LDS in stages of
+// tokens (32 or 64) x EX experts (32, 64 or 128), 4 waves (2 expert halves
+// x 2 token halves, each EX/2 experts x BT/2 tokens).  K goes through LDS in stages of
 // 64 elements, three deep, copied with global_load_lds_dwordx4; rows are
 // 128 bytes with chunk c of row R at slot c ^ ((R >> 1) & 7) (conflict-free
 // operand reads).  Expert rows and token rows past the ends, and the K
 // tail, copy a zeroed page.  Each W_r tile is read by M/BT workgroups and
-// each token row by E/128, all other reuse comes from LDS.
+// each token row by E/EX, all other reuse comes from LDS; the host picks the
+// tile that moves the fewest bytes per CU.
 constexpr int kRtBK = 64;
 constexpr int kRtStages = 3;
-constexpr int kRtExperts = 128;
 
 __device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
 
-template <int BT>
+template <int BT, int EX>
 __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
     float* __restrict__ zero_ptr, size_t zero_words) {
-  constexpr int kRows = kRtExperts + BT;
+  constexpr int kRows = EX + BT;
   constexpr int kStageBytes = kRows * 128;
   constexpr int kCopies = kRows / 8 / 4;     // 1 KB copies per wave per stage
+  constexpr int NTA = EX / 32;               // 16-expert MFMA tiles per wave
   constexpr int NTB = BT / 32;               // 16-token MFMA tiles per wave
+  static_assert(kCopies * 32 == kRows, "copies cover the stage");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   if (zero_ptr != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
     for (size_t i = threadIdx.x; i < zero_words; i += 256) zero_ptr[i] = 0.0f;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lrow = lane >> 3, lpos = lane & 7;
-  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * kRtExperts;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * EX;
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroPage);
-  // copy sources: rows 0..127 experts, 128.. tokens
+  // copy sources: rows 0..EX-1 experts, EX.. tokens
   const uint16_t* src[kCopies];
 #pragma unroll
   for (int c = 0; c < kCopies; ++c) {
     const int R = (wv * kCopies + c) * 8 + lrow;
     const uint16_t* row = nullptr;
-    if (R < kRtExperts) {
+    if (R < EX) {
       if (e0 + R < E) row = wr + (size_t)(e0 + R) * H;
-    } else if (t0 + R - kRtExperts < M) {
-      row = x + (size_t)(t0 + R - kRtExperts) * H;
+    } else if (t0 + R - EX < M) {
+      row = x + (size_t)(t0 + R - EX) * H;
     }
     src[c] = row != nullptr ? row + (lpos ^ rt_swz(R)) * 8 : nullptr;
   }
@@ -197,18 +199,18 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
     }
   };
 
-  const int we = (wv & 1) * 64, wt = (wv >> 1) * (BT / 2);
+  const int we = (wv & 1) * (EX / 2), wt = (wv >> 1) * (BT / 2);
   const int r16 = lane & 15, kg = lane >> 4;
   int abase[2], bbase[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int slot = ((s * 4 + kg) ^ rt_swz(r16)) << 4;
     abase[s] = (we + r16) * 128 + slot;
-    bbase[s] = (kRtExperts + wt + r16) * 128 + slot;
+    bbase[s] = (EX + wt + r16) * 128 + slot;
   }
-  f32x4 acc[4][NTB];
+  f32x4 acc[NTA][NTB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NTA; ++i)
 #pragma unroll
     for (int j = 0; j < NTB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -221,13 +223,13 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
     const uint8_t* sb = lds + (kt % kRtStages) * kStageBytes;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4 af[4], bfr[NTB];
+      u32x4 af[NTA], bfr[NTB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + i * 16 * 128);
+      for (int i = 0; i < NTA; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + i * 16 * 128);
 #pragma unroll
       for (int j = 0; j < NTB; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] + j * 16 * 128);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NTA; ++i)
 #pragma unroll
         for (int j = 0; j < NTB; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
     }
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
     const int t = t0 + wt + 16 * j + r16;
     if (t >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NTA; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = e0 + we + 16 * i + 4 * kg + q;
@@ -294,26 +296,42 @@ hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(route_logits_small_kernel, grid, dim3(256), 0, s, a.x, a.w_router,
                        a.bias, a.M, a.H, a.E, a.logits, a.zero_ptr, a.zero_words);
   } else {
-    // 64-token tiles when they give one workgroup per CU or more, else 32
-    const int ne = ceil_div_host(a.E, kRtExperts);
-    static bool attr_set = false;   // idempotent; racing first calls set the same value
-    if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&route_logits_tiled_kernel<64>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, kRtStages * (kRtExperts + 64) * 128);
-      if (err != hipSuccess) return err;
-      attr_set = true;
-    }
-    if ((long long)ceil_div_host(a.M, 64) * ne >= device_cu_count()) {
-      dim3 grid(ceil_div_host(a.M, 64), ne);
-      hipLaunchKernelGGL(route_logits_tiled_kernel<64>, grid, dim3(256),
-                         kRtStages * (kRtExperts + 64) * 128, s, a.x, a.w_router, a.bias, a.M, a.H,
-                         a.E, a.logits, a.zero_ptr, a.zero_words);
-    } else {
-      dim3 grid(ceil_div_host(a.M, 32), ne);
-      hipLaunchKernelGGL(route_logits_tiled_kernel<32>, grid, dim3(256),
-                         kRtStages * (kRtExperts + 32) * 128, s, a.x, a.w_router, a.bias, a.M, a.H,
-                         a.E, a.logits, a.zero_ptr, a.zero_words);
+    // the (tokens, experts) tile that moves the fewest bytes per CU: rounds
+    // of workgroups over the CUs times each workgroup's rows
+    const int cus = device_cu_count();
+    int best_bt = 64, best_ex = 128;
+    long long best = -1;
+    for (int bt : {32, 64})
+      for (int ex : {32, 64, 128}) {
+        const long long wgs = (long long)ceil_div_host(a.M, bt) * ceil_div_host(a.E, ex);
+        const long long cost = (wgs + cus - 1) / cus * (bt + ex);
+        if (best < 0 || cost < best) { best = cost; best_bt = bt; best_ex = ex; }
+      }
+    dim3 grid(ceil_div_host(a.M, best_bt), ceil_div_host(a.E, best_ex));
+    const size_t lds = (size_t)kRtStages * (best_ex + best_bt) * 128;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, a.x, a.w_router, a.bias, a.M, a.H, a.E,
+                         a.logits, a.zero_ptr, a.zero_words);
+    };
+    switch (best_bt * 1000 + best_ex) {
+      case 32032: go(route_logits_tiled_kernel<32, 32>); break;
+      case 32064: go(route_logits_tiled_kernel<32, 64>); break;
+      case 32128: go(route_logits_tiled_kernel<32, 128>); break;
+      case 64032: go(route_logits_tiled_kernel<64, 32>); break;
+      case 64064: go(route_logits_tiled_kernel<64, 64>); break;
+      default: {
+        // 72 KB of LDS: above the default limit of dynamic LDS
+        static bool attr_set = false;   // idempotent; racing first calls set the same value
+        if (!attr_set) {
+          hipError_t e = hipFuncSetAttribute(
+              reinterpret_cast<const void*>(&route_logits_tiled_kernel<64, 128>),
+              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (e != hipSuccess) return e;
+          attr_set = true;
+        }
+        go(route_logits_tiled_kernel<64, 128>);
+        break;
+      }
     }
   }
   return hipGetLastError();
