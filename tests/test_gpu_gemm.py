@@ -93,7 +93,8 @@ def test_gemms_renormalize_off(B):
                                       ("qwen3_decode", 64, 16), ("qwen15", 16, 16),
                                       ("qwen15", 512, 64), ("wide256", 8, 16),
                                       ("qwen3_decode", 64, 64), ("qwen15", 512, 256),
-                                      ("qwen3_prefill", 4096, 256)])
+                                      ("qwen3_prefill", 4096, 256), ("qwen3_prefill", 4096, 128),
+                                      ("qwen15", 2048, 256), ("wide256", 8192, 128)])
 def test_gemms_full_shapes(name, M, B):
     lay = wl.make_layer(name, M)
     run_case(lay, B, pairs_checked=512)
