@@ -78,17 +78,6 @@ __device__ __forceinline__ int block_scan_exclusive(int v, int* wave_tot, int& t
   return base + incl - v;
 }
 
-// Largest e with boff[e] <= blk; for blk < num_blocks that expert is never
-// empty (an empty expert e has boff[e] == boff[e+1], so e+1 also qualifies).
-__device__ __forceinline__ int expert_of_block(const int* boff, int E, int blk) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (boff[mid] <= blk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 struct Seg {
   int s0, s1;   // this workgroup's pairs
   int w0, w1;   // this wave's pairs
@@ -198,15 +187,14 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
     __builtin_amdgcn_wave_barrier();
   }
 
-  // expert of each block and the pad entries, split over the workgroups
-  const int gtid = gid * kThreads + tid, gstride = G * kThreads;
-  for (int blk = gtid; blk < total_blocks; blk += gstride)
-    expert_ids[blk] = expert_of_block(boff, E, blk);
-  const int nslots = total_blocks * B;
-  for (int pos = gtid; pos < nslots; pos += gstride) {
-    const int blk = pos / B;
-    const int e = expert_of_block(boff, E, blk);
-    if (pos - boff[e] * B >= cnt[e]) sorted[pos] = P;
+  // expert of each block and the pad entries: one wave per expert (waves of
+  // all workgroups), its lanes striding over the expert's blocks and over
+  // the pad slots after its last pair
+  const int gw = gid * kWaves + w, nw = G * kWaves;
+  for (int e = gw; e < E; e += nw) {
+    const int b0 = boff[e], b1 = boff[e + 1];
+    for (int blk = b0 + lane; blk < b1; blk += 64) expert_ids[blk] = e;
+    for (int pos = b0 * B + cnt[e] + lane; pos < b1 * B; pos += 64) sorted[pos] = P;
   }
 }
 
