@@ -13,7 +13,11 @@ Prints ONE JSON line:
                    launch / its mean launch time (HIP events on the stream it
                    runs on), against the MI355X peak
   cpu_baseline     the CPU oracle on a bounded sample of the same workload
-  kernels          mean duration of every kernel of the step (events)
+                   (all BLAS threads, and one thread), with the host CPU model
+  kernels_us       mean duration of every per-step call (events)
+  prefill          the Zipf-routed Qwen3-shaped layer at 4096 tokens timed
+                   the same way, with its own roofline (GEMM 1 flops / its
+                   mean launch time against the bf16 MFMA peak)
   mxfp8            context: moe_forward_mxfp8 (MXFP8 experts and GEMM inputs)
                    on the same shape and batch, the L layers drawn as MXFP8
   quantized        context: moe_forward_quantized (affine 64-element groups,
@@ -42,6 +46,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA, TFLOP/s
 
 DEFAULT_WORKLOAD = ("qwen3_decode", 64)
+PREFILL_WORKLOAD = ("qwen3_prefill", 4096)
 
 
 VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8",
@@ -66,6 +71,11 @@ def parse_args():
                     help="bits:M pairs of the quantized figures (default 4:1,4:4,8:1,8:4)")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the MXFP8 figures")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill object (the Zipf-routed Qwen3-shaped layer at 4096 "
+                         "tokens, timed like the headline)")
+    ap.add_argument("--prefill-layers", type=int, default=4,
+                    help="distinct layers cycled by the prefill object (each 1.2 GB)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration runs)")
     return ap.parse_args()
@@ -146,7 +156,7 @@ def main():
     E, k, H, I = shape.E, shape.top_k, shape.H, shape.I
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lib = moe.library()
+    moe.library()
     stream = torch.cuda.current_stream()
 
     if args.copy_probe:
@@ -156,146 +166,43 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- inputs resident in HBM: L distinct layers, one batch of x ----
     L = max(1, args.layers)
-    layers = [wl.make_device_layer(shape, M, layer=i + 1, device=dev) for i in range(L)]
-    g = torch.Generator(device=dev)
-    g.manual_seed(wl.seed_for(shape, M))
-    x = torch.randn((M, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    ids = torch.empty((M, k), dtype=torch.int32, device=dev)
-    wts = torch.empty((M, k), dtype=torch.float32, device=dev)
-    ws = moe.workspace(M, E, k, H, I, dev)
-    torch.cuda.synchronize()
-
-    def step(i):
-        lay = layers[i % L]
-        return moe.moe_forward(x, lay["w_router"], lay["w13"], lay["w2"], k,
-                               shape.renormalize, logit_bias=lay["logit_bias"], out=out,
-                               topk_ids_out=ids, topk_weights_out=wts, ws=ws, stream=stream)
-
-    # touched experts per layer (from each layer's own routing)
-    touched = []
-    for i in range(L):
-        _, info = step(i)
-        touched.append(int(torch.unique(ids).numel()))
-    torch.cuda.synchronize()
-    mean_touched = float(np.mean(touched))
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    tokens_per_s = M * args.steps / elapsed
-
-    # ---- per-kernel times: the same work as separate C-ABI calls, one step
-    #      at a time: each call is launched `steps` times back to back (layer
-    #      i % L, with that layer's own routing and index lists) between two
-    #      HIP events on the launch stream, so event overhead is amortised ----
-    B = moe.moe_pick_block_m(M, E, k)
-    cap, nbl = moe.align_capacity(M * k, E, B)
-    act = torch.empty((M * k, I), dtype=torch.bfloat16, device=dev)
-    logits = torch.empty((M, E), dtype=torch.float32, device=dev)
-    align_ws = torch.empty(max(moe.moe_align_workspace_size(M, k, E), 16), dtype=torch.uint8,
-                           device=dev)
-    routed = []
-    for i in range(L):
-        lay = layers[i]
-        r_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
-        r_wts = torch.empty((M, k), dtype=torch.float32, device=dev)
-        moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
-                      topk_ids=r_ids, topk_weights=r_wts, logits_out=logits, stream=stream)
-        lists = (torch.empty(cap, dtype=torch.int32, device=dev),
-                 torch.empty(max(nbl, 1), dtype=torch.int32, device=dev),
-                 torch.empty(E + 1, dtype=torch.int32, device=dev),
-                 torch.empty(E, dtype=torch.int32, device=dev))
-        moe.moe_align(r_ids, E, B, *lists, ws=align_ws, stream=stream)
-        routed.append((r_ids, r_wts, lists))
-    scratch_lists = tuple(torch.empty_like(t) for t in routed[0][2])
-
-    def stage(name, i):
-        lay = layers[i % L]
-        r_ids, r_wts, (s_ids, e_ids, b_off, cnt) = routed[i % L]
-        if name == "route":
-            moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
-                          topk_ids=ids, topk_weights=wts, logits_out=logits, stream=stream)
-        elif name == "align":
-            moe.moe_align(r_ids, E, B, *scratch_lists, ws=align_ws, stream=stream)
-        elif name == "gemm1":
-            moe.moe_grouped_gemm_w13_act(x, lay["w13"], s_ids, e_ids, b_off, k, B, act=act,
-                                         stream=stream)
-        else:
-            moe.moe_grouped_gemm_w2_combine(act, lay["w2"], r_wts, s_ids, e_ids, b_off, M, k, B,
-                                            out=out, ws=ws, stream=stream)
-
-    names = ["route", "align", "gemm1", "gemm2"]
-    kern_us = {}
-    for n in names:
-        for i in range(min(args.warmup, 10)):
-            stage(n, i)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            stage(n, i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        kern_us[n] = 1e3 * e0.elapsed_time(e1) / args.steps
-
-    work = algorithmic(shape, M, mean_touched)
-    # the staged calls run the forward's kernel family at the same block size;
-    # at block_m 1 GEMM 1 is the forward's own GEMV (in index-list order),
-    # while the forward's GEMM 2 reads topk_ids and sums in the same launch
-    variant = {1: "pair_gemv", 16: "stream"}.get(B, "tiled")
-    # dominant kernel: GEMM 1 (2/3 of the weight bytes and of the flops)
-    mfma_bound = variant == "tiled" and work["gemm1_flops"] / work["gemm1_bytes"] > \
-        1e3 * BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 0.5
-    t_g1 = kern_us["gemm1"] * 1e-6
-    workload_key = f"{name}_M{M}"
-    if mfma_bound:
-        achieved = work["gemm1_flops"] / t_g1 / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    else:
-        achieved = work["gemm1_bytes"] / t_g1 / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = f"gemm1_{variant}"
-    roof["mean_launch_us"] = round(kern_us["gemm1"], 2)
-    roof["algorithmic_bytes_per_launch"] = int(work["gemm1_bytes"])
-    roof["traffic"] = stored_traffic(workload_key, f"gemm1_{variant}")
-
-    layer_s = ms_per_step * 1e-3
+    m = measure_layer(shape, M, L, args.steps, args.warmup, dev, stream)
+    layers, x, ws, info = m.pop("_layers"), m.pop("_x"), m.pop("_ws"), m.pop("_info")
     result = {
         "metric": "MoE-layer tokens/s",
-        "value": round(tokens_per_s, 1),
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": m["ms_per_layer"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "description": shape.description, "M": M, "E": E,
-                   "top_k": k, "H": H, "I": I, "renormalize": shape.renormalize,
-                   "layers_cycled": L, "block_m": B, "variant": variant,
-                   "forward_variant": VARIANT_NAMES[info["variant"]],
-                   "mean_touched_experts": mean_touched},
-        "layer": {"alg_bytes": int(work["layer_bytes"]), "alg_flops": int(work["layer_flops"]),
-                  "hbm_frac": round(work["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
-                  "mfma_frac": round(work["layer_flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
-        "roofline": roof,
+        "config": m["config"],
+        "layer": m["layer"],
+        "kernels_us": m["kernels_us"],
+        "roofline": m["roofline"],
     }
+
+    # ---- the prefill half of the metric: the Zipf-routed Qwen3-shaped layer
+    #      at 4096 tokens, timed the same way, with its own MFMA roofline ----
+    if not args.no_prefill and (name, M) != PREFILL_WORKLOAD:
+        pname, pM = PREFILL_WORKLOAD
+        pm = measure_layer(wl.WORKLOADS[pname], pM, max(1, min(L, args.prefill_layers)),
+                           args.steps, args.warmup, dev, stream)
+        for key in ("_layers", "_x", "_ws", "_info"):
+            pm.pop(key)
+        result["prefill"] = {"workload": pname, "M": pM, "ms_per_layer": pm["ms_per_layer"],
+                             "tokens_per_s": pm["tokens_per_s"],
+                             "mfma_frac": pm["layer"]["mfma_frac"],
+                             "hbm_frac": pm["layer"]["hbm_frac"], "layer": pm["layer"],
+                             "kernels_us": pm["kernels_us"], "roofline": pm["roofline"],
+                             "config": pm["config"]}
+        torch.cuda.empty_cache()
 
     # ---- decode sweep (same shape, smaller batches) ----
     if not args.no_sweep and name == "qwen3_decode":
@@ -367,6 +274,151 @@ def main():
         result["cpu_baseline"] = cpu_baseline(shape, M, layers[0], x)
 
     print(json.dumps(result), flush=True)
+
+
+def measure_layer(shape, M, L, steps, warmup, dev, stream):
+    """Time moe_forward on one batch of M tokens over L device-resident
+    layers cycled step by step, then each per-step C-ABI call on its own
+    (launched `steps` times back to back between two HIP events on the
+    launch stream, each with its own layer's routing and index lists).
+    Returns tokens/s, ms per layer, the layer's algorithmic fractions, the
+    per-call times and the dominant kernel's (GEMM 1) roofline."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as wl
+    import mixture_experts_ffn_renorm_amd as moe
+
+    name = shape.name
+    E, k, H, I = shape.E, shape.top_k, shape.H, shape.I
+    # ---- inputs resident in HBM: L distinct layers, one batch of x ----
+    layers = [wl.make_device_layer(shape, M, layer=i + 1, device=dev) for i in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_for(shape, M))
+    x = torch.randn((M, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((M, k), dtype=torch.float32, device=dev)
+    ws = moe.workspace(M, E, k, H, I, dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        lay = layers[i % L]
+        return moe.moe_forward(x, lay["w_router"], lay["w13"], lay["w2"], k,
+                               shape.renormalize, logit_bias=lay["logit_bias"], out=out,
+                               topk_ids_out=ids, topk_weights_out=wts, ws=ws, stream=stream)
+
+    # touched experts per layer (from each layer's own routing)
+    touched = []
+    for i in range(L):
+        _, info = step(i)
+        touched.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+    mean_touched = float(np.mean(touched))
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / steps
+    tokens_per_s = M * steps / elapsed
+
+    # ---- per-kernel times: the same work as separate C-ABI calls ----
+    B = moe.moe_pick_block_m(M, E, k)
+    cap, nbl = moe.align_capacity(M * k, E, B)
+    act = torch.empty((M * k, I), dtype=torch.bfloat16, device=dev)
+    logits = torch.empty((M, E), dtype=torch.float32, device=dev)
+    align_ws = torch.empty(max(moe.moe_align_workspace_size(M, k, E), 16), dtype=torch.uint8,
+                           device=dev)
+    routed = []
+    for i in range(L):
+        lay = layers[i]
+        r_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+        r_wts = torch.empty((M, k), dtype=torch.float32, device=dev)
+        moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
+                      topk_ids=r_ids, topk_weights=r_wts, logits_out=logits, stream=stream)
+        lists = (torch.empty(cap, dtype=torch.int32, device=dev),
+                 torch.empty(max(nbl, 1), dtype=torch.int32, device=dev),
+                 torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 torch.empty(E, dtype=torch.int32, device=dev))
+        moe.moe_align(r_ids, E, B, *lists, ws=align_ws, stream=stream)
+        routed.append((r_ids, r_wts, lists))
+    scratch_lists = tuple(torch.empty_like(t) for t in routed[0][2])
+
+    def stage(sname, i):
+        lay = layers[i % L]
+        r_ids, r_wts, (s_ids, e_ids, b_off, cnt) = routed[i % L]
+        if sname == "route":
+            moe.moe_route(x, lay["w_router"], k, shape.renormalize, logit_bias=lay["logit_bias"],
+                          topk_ids=ids, topk_weights=wts, logits_out=logits, stream=stream)
+        elif sname == "align":
+            moe.moe_align(r_ids, E, B, *scratch_lists, ws=align_ws, stream=stream)
+        elif sname == "gemm1":
+            moe.moe_grouped_gemm_w13_act(x, lay["w13"], s_ids, e_ids, b_off, k, B, act=act,
+                                         stream=stream)
+        else:
+            moe.moe_grouped_gemm_w2_combine(act, lay["w2"], r_wts, s_ids, e_ids, b_off, M, k, B,
+                                            out=out, ws=ws, stream=stream)
+
+    kern_us = {}
+    for n in ("route", "align", "gemm1", "gemm2"):
+        for i in range(min(warmup, 10)):
+            stage(n, i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            stage(n, i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern_us[n] = 1e3 * e0.elapsed_time(e1) / steps
+    del routed, scratch_lists, act
+
+    work = algorithmic(shape, M, mean_touched)
+    # the staged calls run the forward's kernel family at the same block size;
+    # at block_m 1 GEMM 1 is the forward's own GEMV (in index-list order),
+    # while the forward's GEMM 2 reads topk_ids and sums in the same launch
+    variant = {1: "pair_gemv", 16: "stream"}.get(B, "tiled")
+    # dominant kernel: GEMM 1 (2/3 of the weight bytes and of the flops)
+    mfma_bound = variant == "tiled" and work["gemm1_flops"] / work["gemm1_bytes"] > \
+        1e3 * BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 0.5
+    t_g1 = kern_us["gemm1"] * 1e-6
+    workload_key = f"{name}_M{M}"
+    if mfma_bound:
+        achieved = work["gemm1_flops"] / t_g1 / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        roof["algorithmic_flops_per_launch"] = int(work["gemm1_flops"])
+    else:
+        achieved = work["gemm1_bytes"] / t_g1 / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = f"gemm1_{variant}"
+    roof["mean_launch_us"] = round(kern_us["gemm1"], 2)
+    roof["algorithmic_bytes_per_launch"] = int(work["gemm1_bytes"])
+    roof["traffic"] = stored_traffic(workload_key, f"gemm1_{variant}")
+
+    layer_s = ms_per_step * 1e-3
+    return {
+        "tokens_per_s": round(tokens_per_s, 1),
+        "ms_per_layer": round(ms_per_step, 5),
+        "config": {"workload": name, "description": shape.description, "M": M, "E": E,
+                   "top_k": k, "H": H, "I": I, "renormalize": shape.renormalize,
+                   "layers_cycled": L, "block_m": B, "variant": variant,
+                   "forward_variant": VARIANT_NAMES[info["variant"]],
+                   "mean_touched_experts": mean_touched},
+        "layer": {"alg_bytes": int(work["layer_bytes"]), "alg_flops": int(work["layer_flops"]),
+                  "hbm_frac": round(work["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(work["layer_flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": roof,
+        "_layers": layers, "_x": x, "_ws": ws, "_info": info,
+    }
 
 
 def quantized_alg_bytes(shape, M, bits, touched):
@@ -491,11 +543,25 @@ def quantized_figures(shape, L, x, dev, reps, sizes):
     return res
 
 
-def cpu_baseline(shape, M, lay, x, min_s=10.0, max_reps=40):
+def cpu_model_name() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, M, lay, x, min_s=8.0, max_reps=40):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: layer 0 of the cycle, the first S <= 64 tokens of the batch,
     the whole forward repeated until about `min_s` seconds of CPU work have
-    run (at most `max_reps` times); tokens/s = reps * S / wall time."""
+    run (at most `max_reps` times); tokens/s = reps * S / wall time.  Timed
+    twice: with numpy's BLAS on all its threads (`value`, `cores`) and
+    limited to one thread (`value_1thread`)."""
     import numpy as np
     import torch
 
@@ -510,25 +576,37 @@ def cpu_baseline(shape, M, lay, x, min_s=10.0, max_reps=40):
                 logit_bias=None if lay["logit_bias"] is None else lay["logit_bias"].cpu().numpy(),
                 M=S, E=shape.E, top_k=shape.top_k, H=shape.H, I=shape.I,
                 renormalize=shape.renormalize)
+
+    def timed():
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            mo.forward(host)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s or reps >= max_reps:
+                return reps, dt
+
     threads = None
+    limits = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max((p.get("num_threads") or 1) for p in threadpool_info()) or None
+        limits = threadpool_limits
     except Exception:
         pass
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        mo.forward(host)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_s or reps >= max_reps:
-            break
-    return {"value": round(reps * S / dt, 3), "unit": "tokens/s",
-            "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": f"{S} tokens of layer 0 ({shape.name}, M={M}), the whole oracle forward "
-                      f"run {reps} times; numpy float64, {dt:.2f} s wall",
-            "host_cpus": os.cpu_count()}
+    reps, dt = timed()
+    res = {"value": round(reps * S / dt, 3), "unit": "tokens/s",
+           "cores": threads or os.cpu_count(), "kind": "oracle",
+           "sample": f"{S} tokens of layer 0 ({shape.name}, M={M}), the whole oracle forward "
+                     f"run {reps} times; numpy float64, {dt:.2f} s wall",
+           "host_cpus": os.cpu_count(), "cpu_model": cpu_model_name()}
+    if limits is not None:
+        with limits(limits=1):
+            reps1, dt1 = timed()
+        res["value_1thread"] = round(reps1 * S / dt1, 3)
+        res["sample_1thread"] = f"the same sample run {reps1} times on one thread, {dt1:.2f} s wall"
+    return res
 
 
 if __name__ == "__main__":

@@ -228,6 +228,30 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
                 void* workspace, size_t ws_bytes, moe_dispatch_info* info, void* stream);
 
 /*
+ * Where moe_forward leaves the index lists of a batch in its workspace
+ * (host struct): byte offsets from the workspace start, valid after a
+ * moe_forward call with the same (M, E, top_k, H, I) on that workspace
+ * has completed.  The lists are the ones of moe_align (page "Mixture of
+ * Experts in vLLM ...", sub-section "The two index lists") for the
+ * routing moe_forward chose, with block_m = moe_pick_block_m(M, E, top_k);
+ * only the first num_blocks entries of expert_ids and num_blocks*block_m of
+ * sorted_token_ids are written (num_blocks = expert_block_offsets[E]).
+ * A caller can read them back to see how the batch was dispatched.
+ */
+typedef struct moe_forward_lists {
+  int block_m;                  /* rows per block of the lists                */
+  int sorted;                   /* 0: this M runs per-pair GEMVs, no lists     */
+  size_t sorted_token_ids;      /* int32 [M*top_k + min(E, P)*(block_m-1)]    */
+  size_t expert_ids;            /* int32 [ceil(P/block_m) + min(E, P)]        */
+  size_t expert_block_offsets;  /* int32 [E+1]                                */
+  size_t expert_counts;         /* int32 [E]                                  */
+} moe_forward_lists;
+
+/* Fills *out for a batch of M tokens; returns MOE_OK, or a negative status
+ * (nothing written) for unsupported sizes or a null out. */
+int moe_forward_list_offsets(int M, int E, int top_k, int H, int I, moe_forward_lists* out);
+
+/*
  * Group-quantized expert weights (host struct of device pointers): the
  * affine group format in the MLX part of the page "SGLang issue #22283"
  * (GitHub thread): its kernels read 64-element-group, 4-bit weights

@@ -9,8 +9,8 @@ binding works but every call raises.
 Function names match the C ABI: moe_route, moe_align,
 moe_grouped_gemm_w13_act, moe_grouped_gemm_w2_combine, moe_forward,
 moe_forward_quantized, moe_forward_mxfp8, moe_mx_quantize, plus
-moe_workspace_size, moe_mx_workspace_size, moe_pick_block_m and
-moe_strerror.
+moe_workspace_size, moe_mx_workspace_size, moe_pick_block_m,
+moe_forward_list_offsets and moe_strerror.
 """
 
 from __future__ import annotations
@@ -49,6 +49,13 @@ class DispatchInfo(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class ForwardLists(ctypes.Structure):
+    """moe_forward_lists: where moe_forward leaves its index lists."""
+    _fields_ = [("block_m", _c_int), ("sorted", _c_int), ("sorted_token_ids", _c_size_t),
+                ("expert_ids", _c_size_t), ("expert_block_offsets", _c_size_t),
+                ("expert_counts", _c_size_t)]
+
+
 class MxWeights(ctypes.Structure):
     """moe_mx_weights: four device pointers (E4M3 codes and E8M0 scales)."""
     _fields_ = [("w13_codes", _c_void_p), ("w13_scales", _c_void_p),
@@ -80,6 +87,7 @@ _SIGNATURES = {
     "moe_forward": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
                     [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                      ctypes.POINTER(DispatchInfo), _c_void_p]),
+    "moe_forward_list_offsets": (_c_int, [_c_int] * 5 + [ctypes.POINTER(ForwardLists)]),
     "moe_mx_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "moe_mx_workspace_size": (_c_size_t, [_c_int] * 5),
     "moe_forward_mxfp8": (_c_int, [_c_void_p] * 3 + [ctypes.POINTER(MxWeights)] + [_c_int] * 6 +
@@ -331,6 +339,34 @@ def moe_forward(x, w_router, w13, w2, top_k: int, renormalize: bool = True,
         _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
     _raise("moe_forward", st)
     return out, info.as_dict()
+
+
+def moe_forward_list_offsets(M: int, E: int, top_k: int, H: int, I: int) -> dict:
+    """Byte offsets in moe_forward's workspace of the index lists it builds
+    for a batch of M tokens, with their block size (``sorted`` 0: none)."""
+    lists = ForwardLists()
+    _raise("moe_forward_list_offsets",
+           library().moe_forward_list_offsets(M, E, top_k, H, I, ctypes.byref(lists)))
+    return {f: getattr(lists, f) for f, _ in lists._fields_}
+
+
+def forward_lists(ws, M: int, E: int, top_k: int, H: int, I: int):
+    """The index lists moe_forward left in workspace tensor ``ws`` (after a
+    completed call with these sizes), as int32 views: (sorted_token_ids,
+    expert_ids, expert_block_offsets, expert_counts, block_m).  Only the
+    first num_blocks*block_m / num_blocks entries of the first two hold
+    data (num_blocks = expert_block_offsets[E])."""
+    torch = _torch()
+    o = moe_forward_list_offsets(M, E, top_k, H, I)
+    if not o["sorted"]:
+        raise ValueError("moe_forward builds no index lists for this batch size")
+    cap, nbl = align_capacity(M * top_k, E, o["block_m"])
+
+    def view(off, n):
+        return ws[off:off + 4 * n].view(torch.int32)
+
+    return (view(o["sorted_token_ids"], cap), view(o["expert_ids"], nbl),
+            view(o["expert_block_offsets"], E + 1), view(o["expert_counts"], E), o["block_m"])
 
 
 def moe_forward_quantized(x, w_router, qweights: dict, top_k: int, renormalize: bool = True,

@@ -214,8 +214,9 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
 // behind each other), then the index lists built by the workgroup that
 // arrives last.  Each workgroup publishes its expert ids with agent-coherent
 // stores, waits for them, and counts its arrival in *arrivals (zeroed by the
-// router-logits kernel on the same stream); the last one reads all P ids
-// back with agent-coherent loads.  A lone workgroup keeps its ids in LDS.
+// router-logits kernel on the same stream) with an agent-scope
+// acquire-release add; the last one reads all P ids back with
+// agent-coherent loads.  A lone workgroup keeps its ids in LDS.
 __global__ __launch_bounds__(kThreads) void route_topk_align_kernel(
     const float* __restrict__ logits, int M, int E, int top_k, int renormalize, int B,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
@@ -240,9 +241,15 @@ __global__ __launch_bounds__(kThreads) void route_topk_align_kernel(
     }
   }
   if (gridDim.x > 1) {
+    // Every wave's id stores have completed before the workgroup barrier;
+    // the arrival is an agent-scope acquire-release add, so each workgroup's
+    // stores happen before its arrival, and the last arrival (which then
+    // reads every workgroup's ids) happens after all of them.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+               (int)gridDim.x - 1;
     __syncthreads();
     if (!s_last) return;
     for (int i = threadIdx.x; i < P; i += kThreads)
@@ -267,14 +274,10 @@ static_assert(kFusedRouteMaxLds <= 100 * 1024, "fused top-k + align LDS");
 hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32_t* arrivals,
                                    hipStream_t s) {
   const size_t lds = route_topk_align_lds(r.M * r.top_k, r.E);
-  static bool attr_set = false;   // idempotent; racing first calls set the same value
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_topk_align_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)kFusedRouteMaxLds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static bool lds_set[kMaxDevices] = {};
+  const hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&route_topk_align_kernel),
+                                            (int)kFusedRouteMaxLds, lds_set);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_topk_align_kernel, dim3(ceil_div_host(r.M, kTopkWaves)), dim3(kThreads),
                      lds, s, r.logits, r.M, r.E, r.top_k, r.renormalize, a.block_m, r.topk_ids,
                      r.topk_weights, a.sorted_token_ids, a.expert_ids, a.expert_block_offsets,

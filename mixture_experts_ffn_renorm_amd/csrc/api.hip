@@ -224,6 +224,21 @@ int moe_pick_block_m(int M, int E, int top_k) {
   return 128;
 }
 
+int moe_forward_list_offsets(int M, int E, int top_k, int H, int I, moe_forward_lists* out) {
+  const int st = check_sizes(M, E, top_k, H, I);
+  if (st != MOE_OK) return st;
+  if (out == nullptr) return MOE_ERR_INVALID_ARG;
+  const int B = moe_pick_block_m(M, E, top_k);
+  const Layout L = forward_layout(M, E, top_k, H, I, B);
+  out->block_m = B;
+  out->sorted = (M > 0 && !per_pair_gemv(M, top_k, E)) ? 1 : 0;
+  out->sorted_token_ids = L.sorted;
+  out->expert_ids = L.eids;
+  out->expert_block_offsets = L.boff;
+  out->expert_counts = L.counts;
+  return MOE_OK;
+}
+
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* logit_bias, int M,
               int H, int E, int top_k, int renormalize, int32_t* topk_ids,
               float* topk_weights, float* logits_out, void* workspace, size_t ws_bytes,
@@ -501,7 +516,8 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
   if (!mx_sizes_ok(H, I)) return MOE_ERR_UNSUPPORTED;
   const int B = mx_block_m(M, E, top_k);
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
-  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 2 + 2 + kGemm2Launches);
+  // quantize x, GEMM 1, quantize act, then GEMM 2 and its per-token sum
+  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 3 + kGemm2Launches);
   if (info != nullptr) info->variant = B == 16 ? MOE_VARIANT_STREAM_MXFP8 : MOE_VARIANT_TILED_MXFP8;
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !out || !w->w13_codes || !w->w13_scales || !w->w2_codes ||

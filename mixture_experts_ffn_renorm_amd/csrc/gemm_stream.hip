@@ -9,12 +9,12 @@
 // block and 32 weight rows:
 //   GEMM 1: 16 gate rows and the matching 16 up rows of W13[e] -> 16 act
 //           columns (SiLU(gate) * up), rows p of act in pair order;
-//   GEMM 2: 32 rows of W2[e] -> 32 output columns; the epilogue scales by
-//           topk_weights[p], stores the fp32 partial row p, and the last of
-//           the top_k producers of a (token, 32 columns) piece adds the
-//           token's partial rows in slot order and writes bf16 (page
-//           sections "Put the results back, and combine them per token" and
-//           "The rest of the layer stays in pair order").
+//   GEMM 2: 64 rows of W2[e] -> 64 output columns; the epilogue scales by
+//           topk_weights[p] and stores the fp32 partial row p, and a second
+//           small kernel adds each token's top_k partial rows in slot order
+//           and writes bf16 (page sections "The rest of the layer stays in
+//           pair order" and "Put the results back, and combine them per
+//           token"); see the GEMM 2 notes below.
 //
 // Persistent workgroups (two per CU) walk the tiles; each XCD takes one
 // contiguous range of tiles, so the tiles of one block (same gathered rows)
@@ -53,7 +53,6 @@ constexpr int kStages = 3;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStageBytes = (kWRows + kBM) * kRowB;       // 24 KB
-constexpr int kRingBytes = kStages * kStageBytes;          // 72 KB
 constexpr int kWCopies = kWRows / 2 / kWaves;              // 1 KB copies per wave: weights (4)
 constexpr int kXCopies = kBM / 2 / kWaves;                 //                       pair rows (2)
 constexpr int kCopies = kWCopies + kXCopies;
@@ -280,7 +279,6 @@ constexpr int kStages = 3;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kStageBytes = (kWRows + kBM) * kRowB;         // 20 KB
-constexpr int kRingBytes = kStages * kStageBytes;            // 60 KB
 constexpr int kWCopies = kWRows / 4 / kWaves;               // 1 KB = 4 rows; per wave (4)
 constexpr int kXCopies = kBM / 4 / kWaves;                  // (1)
 constexpr int kCopies = kWCopies + kXCopies;
@@ -472,13 +470,10 @@ hipError_t launch_gemm1(const moe_host::GemmArgs& a, hipStream_t s) {
   long long grid = std::min<long long>(tiles, 2LL * moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
   constexpr int kRing = kStages * stage_bytes<kMX>();
-  static bool attr_set = false;   // idempotent; racing first calls set the same value
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm1_stream_kernel<kMX>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRing);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static bool lds_set[moe_host::kMaxDevices] = {};
+  const hipError_t err = moe_host::ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&gemm1_stream_kernel<kMX>), kRing, lds_set);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(gemm1_stream_kernel<kMX>, dim3((unsigned)grid), dim3(kThreads), kRing, s, prm);
   return hipGetLastError();
 }
@@ -505,16 +500,13 @@ hipError_t launch_gemm2(const moe_host::GemmArgs& a, hipStream_t s) {
   long long grid = std::min<long long>(tiles, 2LL * moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
   constexpr int kRing = ring2::kStages * ring2::stage_bytes<kMX>();
-  static bool attr_set = false;   // idempotent; racing first calls set the same value
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&ring2::gemm2_ring_kernel<kMX>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRing);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static bool lds_set[moe_host::kMaxDevices] = {};
+  hipError_t err = moe_host::ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&ring2::gemm2_ring_kernel<kMX>), kRing, lds_set);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ring2::gemm2_ring_kernel<kMX>, dim3((unsigned)grid), dim3(ring2::kThreads),
                      kRing, s, prm);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   return moe_host::launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
 }

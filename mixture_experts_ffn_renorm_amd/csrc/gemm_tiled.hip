@@ -77,7 +77,6 @@ namespace {
 
 constexpr int kBK = 64;          // k elements per stage = 128 bytes per row
 constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kRowBytes = kBK * 2;
 constexpr int kMeta = 5;         // tile metadata buffers (pair ids, expert)
 
@@ -174,7 +173,6 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   const int lrow = lane >> 3, lpos = lane & 7;
   // copy wave index (kPC: waves kWaves.. copy, waves 0..kWaves-1 multiply)
   const bool copier = !kPC || wv >= kWaves;
-  const bool mfma_wave = !kPC || wv < kWaves;
   const int cw = kPC ? wv - kWaves : wv;
 
   // ---- metadata copies of tile i into buffer i % kMeta ----
@@ -581,14 +579,10 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* ou
   long long grid = std::min<long long>(tiles, moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
   const size_t lds = C::kRingBytes;
-  static bool attr_set = false;   // idempotent; racing first calls set the same value
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX, kPC>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static bool lds_set[moe_host::kMaxDevices] = {};
+  const hipError_t err = moe_host::ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX, kPC>), (int)lds, lds_set);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX, kPC>), dim3((unsigned)grid), dim3(C::kThreadsT),
                      lds, s, prm);
   return hipGetLastError();

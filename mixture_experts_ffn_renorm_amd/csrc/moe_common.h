@@ -413,4 +413,19 @@ constexpr int kPairGemvK = 2048;        // K elements per lane-pass of the per-p
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Raises a kernel's dynamic-LDS limit on the current device once; `done`
+// is that kernel's own per-device flag array.  Concurrent first calls on one
+// device both set the same value.
+constexpr int kMaxDevices = 64;
+inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, bool (&done)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  if (known && done[dev]) return hipSuccess;
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess && known) done[dev] = true;
+  return err;
+}
+
 }  // namespace moe_host

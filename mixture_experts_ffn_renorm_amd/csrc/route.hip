@@ -321,14 +321,10 @@ hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
       case 64064: go(route_logits_tiled_kernel<64, 64>); break;
       default: {
         // 72 KB of LDS: above the default limit of dynamic LDS
-        static bool attr_set = false;   // idempotent; racing first calls set the same value
-        if (!attr_set) {
-          hipError_t e = hipFuncSetAttribute(
-              reinterpret_cast<const void*>(&route_logits_tiled_kernel<64, 128>),
-              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-          if (e != hipSuccess) return e;
-          attr_set = true;
-        }
+        static bool lds_set[kMaxDevices] = {};
+        const hipError_t e = ensure_dynamic_lds(
+            reinterpret_cast<const void*>(&route_logits_tiled_kernel<64, 128>), (int)lds, lds_set);
+        if (e != hipSuccess) return e;
         go(route_logits_tiled_kernel<64, 128>);
         break;
       }

@@ -339,19 +339,37 @@ def make_device_quantized_layer(shape: LayerShape | str, M: int, bits: int, laye
 MX_BLOCK = 32
 
 
+# E4M3 codes other than the two NaN codes (0x7F, 0xFF): zero and negative
+# zero, the subnormals, every exponent field 1..15 and +-448, in code order.
+MX_FINITE_CODES = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def mx_code_rms() -> float:
+    """Root mean square of the E4M3 values when the code is uniform over
+    MX_FINITE_CODES (codes decoded from their bit fields: bias 7, exponent 0
+    subnormal with steps of 2^-9)."""
+    c = MX_FINITE_CODES.astype(np.int64)
+    e, m = (c >> 3) & 0xF, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return float(np.sqrt(np.mean(mag * mag)))
+
+
+def mx_scale_base(K: int) -> int:
+    """E8M0 code that gives weights of uniform random finite codes a spread
+    near 1/sqrt(K): 127 + round(log2(1 / (rms * sqrt(K))))."""
+    return 127 + int(round(math.log2(1.0 / (mx_code_rms() * math.sqrt(K)))))
+
+
 def _mx_matrix(rows: int, K: int, seq: np.random.SeedSequence):
     """Random MXFP8 codes and scales of one expert matrix [rows, K]: E4M3
-    bytes with a random sign, exponent field uniform over 4..9 and mantissa
-    uniform over 0..7 (magnitudes 1/8 .. 3.75, no NaN codes), and per
-    32-element block an E8M0 scale code 127 - round(log2 sqrt K) - 1 + {-1,
-    0, 1}, so that the weights have a spread near 1/sqrt(K)."""
+    bytes uniform over every finite code (zeros, subnormals, all exponent
+    fields, +-448; no NaN), and per 32-element block an E8M0 scale
+    mx_scale_base(K) + {-1, 0, 1}, so that the weights spread near
+    1/sqrt(K) with the heavy tail of the full E4M3 range."""
     rng = np.random.Generator(np.random.PCG64(seq))
-    sign = rng.integers(0, 2, size=(rows, K), dtype=np.uint8) << 7
-    expo = rng.integers(4, 10, size=(rows, K), dtype=np.uint8) << 3
-    mant = rng.integers(0, 8, size=(rows, K), dtype=np.uint8)
-    base = 127 - int(round(math.log2(math.sqrt(K)))) - 1
-    scales = (base + rng.integers(-1, 2, size=(rows, K // MX_BLOCK))).astype(np.uint8)
-    return (sign | expo | mant).astype(np.uint8), scales
+    codes = MX_FINITE_CODES[rng.integers(0, MX_FINITE_CODES.size, size=(rows, K))]
+    scales = (mx_scale_base(K) + rng.integers(-1, 2, size=(rows, K // MX_BLOCK))).astype(np.uint8)
+    return codes, scales
 
 
 def make_mx_layer(shape: LayerShape | str, M: int, layer: int = 0,
@@ -407,11 +425,10 @@ def make_device_mx_layer(shape: LayerShape | str, M: int, layer: int, device) ->
     w_router = (torch.randn((E, H), generator=g, device=device) * rstd).to(torch.bfloat16)
     w = {}
     for name, rows, K in (("w13", 2 * I, H), ("w2", H, I)):
-        sign = torch.randint(0, 2, (E, rows, K), generator=g, device=device, dtype=torch.uint8)
-        expo = torch.randint(4, 10, (E, rows, K), generator=g, device=device, dtype=torch.uint8)
-        mant = torch.randint(0, 8, (E, rows, K), generator=g, device=device, dtype=torch.uint8)
-        w[name + "_codes"] = (sign << 7) | (expo << 3) | mant
-        base = 127 - int(round(math.log2(math.sqrt(K)))) - 1
+        # uniform over the 254 finite codes: draw 0..253 and step over 0x7F
+        r = torch.randint(0, 254, (E, rows, K), generator=g, device=device, dtype=torch.int32)
+        w[name + "_codes"] = (r + (r >= 0x7F).to(torch.int32)).to(torch.uint8)
+        base = mx_scale_base(K)
         w[name + "_scales"] = (base + torch.randint(-1, 2, (E, rows, K // MX_BLOCK), generator=g,
                                                     device=device)).to(torch.uint8)
     bias = None

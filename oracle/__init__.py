@@ -16,6 +16,8 @@ from .moe_oracle import (  # noqa: F401
     widen_bf16,
     router_logits,
     route,
+    softmax_probs,
+    weights_of,
     topk_margin,
     align,
     swiglu,
@@ -27,6 +29,7 @@ from .moe_oracle import (  # noqa: F401
     unpack_codes,
     dequantize_affine,
     forward_quantized,
+    dequantized_experts,
     QUANT_GROUP,
     MX_BLOCK,
     e4m3_value,
@@ -36,4 +39,5 @@ from .moe_oracle import (  # noqa: F401
     mx_dequantize,
     round_to_bf16_via_f32,
     forward_mxfp8,
+    mx_layer_forward,
 )

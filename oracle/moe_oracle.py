@@ -75,21 +75,35 @@ def route(x: np.ndarray, w_router: np.ndarray, top_k: int, renormalize: bool,
     M, E = logits.shape
     assert 1 <= top_k <= E
     logits_f32 = logits.astype(np.float32)
-    # 1. softmax over all experts
-    shifted = logits - logits.max(axis=1, keepdims=True)
-    ex = np.exp(shifted)
-    prob = ex / ex.sum(axis=1, keepdims=True)
     # 2. the k largest, descending; ties -> lower id.  Softmax is strictly
     #    increasing, so ordering the float32 logits orders the probabilities.
     idx = np.broadcast_to(np.arange(E), (M, E))
     order = np.lexsort((idx, -logits_f32), axis=1)
     topk_ids = order[:, :top_k].astype(np.int32)
-    w = np.take_along_axis(prob, topk_ids.astype(np.int64), axis=1)
-    # 3. renormalize
-    if renormalize:
-        w = w / w.sum(axis=1, keepdims=True)
+    # 1. and 3.: softmax over all experts, the kept probabilities, renormalize
+    w = weights_of(logits, topk_ids, renormalize)
     return dict(topk_ids=topk_ids, topk_weights=w, logits=logits,
                 logits_f32=logits_f32, margin=topk_margin(logits_f32, top_k))
+
+
+def softmax_probs(logits: np.ndarray) -> np.ndarray:
+    """Softmax over all E experts of each row of float64 logits."""
+    shifted = logits - logits.max(axis=1, keepdims=True)
+    ex = np.exp(shifted)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def weights_of(logits: np.ndarray, ids: np.ndarray, renormalize: bool) -> np.ndarray:
+    """Router weights of the experts `ids` [M, k] of each token: their
+    softmax probabilities (softmax over all E), rescaled to sum 1 when
+    renormalize is set.  For the top-k ids this is the router's output; for
+    other ids (another implementation's choice among near-tied experts) it
+    is what the same router step gives those experts."""
+    prob = softmax_probs(np.asarray(logits, dtype=np.float64))
+    w = np.take_along_axis(prob, np.asarray(ids, dtype=np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
 
 
 # ---------------------------------------------------------------------------
@@ -327,9 +341,7 @@ def forward_quantized(layer: dict, tokens: np.ndarray | None = None) -> dict:
     (the router stays bf16), then the same grouped expert FFNs and weighted
     sum on the dequantized W13 and W2."""
     x = layer["x"]
-    M, H = x.shape
-    I = layer["I"]
-    bits = layer["bits"]
+    M = x.shape[0]
     tokens = np.arange(M) if tokens is None else np.asarray(tokens)
     r = route(x[tokens], layer["w_router"], layer["top_k"], layer["renormalize"],
               layer.get("logit_bias"))
@@ -337,9 +349,16 @@ def forward_quantized(layer: dict, tokens: np.ndarray | None = None) -> dict:
     wts = np.zeros((M, layer["top_k"]))
     ids[tokens] = r["topk_ids"]
     wts[tokens] = r["topk_weights"]
-    w13 = DequantizedExperts(layer["w13_q"], layer["w13_scales"], layer["w13_biases"], bits, H)
-    w2 = DequantizedExperts(layer["w2_q"], layer["w2_scales"], layer["w2_biases"], bits, I)
+    w13, w2 = dequantized_experts(layer)
     return dict(route=r, tokens=tokens, y=layer_forward(x, w13, w2, ids, wts, tokens))
+
+
+def dequantized_experts(layer: dict):
+    """(W13, W2) of a group-quantized layer as on-demand dequantized expert
+    matrices, for ``layer_forward``."""
+    H, I, bits = layer["H"], layer["I"], layer["bits"]
+    return (DequantizedExperts(layer["w13_q"], layer["w13_scales"], layer["w13_biases"], bits, H),
+            DequantizedExperts(layer["w2_q"], layer["w2_scales"], layer["w2_biases"], bits, I))
 
 
 # ---------------------------------------------------------------------------
@@ -445,16 +464,31 @@ def forward_mxfp8(layer: dict, tokens: np.ndarray | None = None) -> dict:
     wts = np.zeros((M, k))
     ids[tokens] = r["topk_ids"]
     wts[tokens] = r["topk_weights"]
+    y, xq, xs = mx_layer_forward(layer, ids, wts, tokens)
+    return dict(route=r, tokens=tokens, y=y, x_codes=xq, x_scales=xs)
+
+
+def mx_layer_forward(layer: dict, topk_ids: np.ndarray, topk_weights: np.ndarray,
+                     tokens: np.ndarray | None = None):
+    """The expert part of the MXFP8 layer for given routing (ids and
+    weights [M, k]): x quantized to MXFP8, per pair h = W13_e deq(q(x_t)),
+    act = SwiGLU(h) stored as bf16 then quantized, y_p = W2_e deq(q(act_p)),
+    and the weighted top-k sum of the requested tokens.  Returns
+    (y float64 [T, H], x codes, x scales)."""
+    x = layer["x"]
+    M, H = x.shape
+    I, k = layer["I"], layer["top_k"]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
     xq, xs = mx_quantize(widen_bf16(x))
     X = mx_dequantize(xq, xs)
     pos = np.full(M, -1)
     pos[tokens] = np.arange(tokens.size)
     slots = np.zeros((tokens.size, k, H))
-    for e, ts, js in _pairs_by_expert(ids, tokens):
+    for e, ts, js in _pairs_by_expert(topk_ids, tokens):
         W13 = mx_dequantize(layer["w13_codes"][e], layer["w13_scales"][e])
         W2 = mx_dequantize(layer["w2_codes"][e], layer["w2_scales"][e])
         act = widen_bf16(round_to_bf16_via_f32(swiglu(X[ts] @ W13.T, I)))
         aq, asc = mx_quantize(act)
         slots[pos[ts], js] = mx_dequantize(aq, asc) @ W2.T
-    y = np.einsum("tk,tkh->th", wts[tokens], slots)
-    return dict(route=r, tokens=tokens, y=y, x_codes=xq, x_scales=xs)
+    y = np.einsum("tk,tkh->th", np.asarray(topk_weights, dtype=np.float64)[tokens], slots)
+    return y, xq, xs

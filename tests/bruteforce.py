@@ -90,3 +90,51 @@ def layer(layer_np: dict):
         w_all.append(w)
         y_all.append(y)
     return ids_all, w_all, y_all
+
+
+def expert_act(xv, w13_e):
+    """The activation row of one (token, expert) pair: SiLU(gate) * up."""
+    I = len(w13_e) // 2
+    gate = [dot(w13_e[n], xv) for n in range(I)]
+    up = [dot(w13_e[I + n], xv) for n in range(I)]
+    return [gate[n] * sigmoid(gate[n]) * up[n] for n in range(I)]
+
+
+def weights_of_ids(xv, wr, ids, renormalize, bias=None):
+    """Router weights of the given experts (not necessarily the top-k):
+    their softmax probabilities over all experts, optionally rescaled to
+    sum 1."""
+    E = len(wr)
+    logits = [dot(wr[e], xv) + (0.0 if bias is None else float(bias[e])) for e in range(E)]
+    mx = max(logits)
+    ex = [math.exp(l - mx) for l in logits]
+    s = math.fsum(ex)
+    w = [ex[e] / s for e in ids]
+    if renormalize:
+        tot = math.fsum(w)
+        w = [v / tot for v in w]
+    return w
+
+
+def pair_rows(X, W13, ids):
+    """Activation rows of every pair, listed by pair id: for token t (rows
+    of X in order) and slot j (columns of ids[t] in order), the row
+    SiLU(gate) * up of expert ids[t][j] on x_t.  Returns a list of rows."""
+    rows = []
+    for t, xv in enumerate(X):
+        for e in ids[t]:
+            rows.append(expert_act(xv, W13[e]))
+    return rows
+
+
+def combine(A, W2, ids, weights):
+    """Per-token output from given activation rows A (listed by pair id):
+    out_t = sum over slots j of weights[t][j] * (W2 of expert ids[t][j]) a,
+    with a the row of pair number t * len(ids[t]) + j."""
+    out = []
+    for t, (row_ids, row_w) in enumerate(zip(ids, weights)):
+        k = len(row_ids)
+        H = len(W2[row_ids[0]])
+        ys = [[dot(W2[e][h], A[t * k + j]) for h in range(H)] for j, e in enumerate(row_ids)]
+        out.append([math.fsum(row_w[j] * ys[j][h] for j in range(k)) for h in range(H)])
+    return out

@@ -5,6 +5,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import moe_oracle as mo
+
 # Layer outputs: bf16 inputs, fp32 accumulation, bf16 activations and output.
 MAX_ABS_REL = 2e-2       # max |y - ref| <= 2e-2 * max |ref|
 MEAN_REL = 5e-3          # sum |y - ref| <= 5e-3 * sum |ref|
@@ -59,3 +61,45 @@ def sample_tokens(M: int, n: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     t = rng.choice(M, size=n - 2, replace=False)
     return np.unique(np.concatenate([[0, M - 1], t]))
+
+
+def check_routing(ids: np.ndarray, wts: np.ndarray, r: dict, renormalize: bool) -> np.ndarray:
+    """Routing of the sampled tokens against the oracle's route `r` of the
+    same tokens.  Ids are unique where the top-k logit margin exceeds MARGIN
+    and must match there bit for bit; on every token the choice must be a
+    valid ordered top-k up to near ties (distinct ids in range, each chosen
+    expert's oracle logit within 2*MARGIN of the k-th largest, every expert
+    clearly above the k-th chosen, slots in descending logit order up to
+    2*MARGIN).  The weights of every token must equal, within WEIGHT_TOL,
+    what the oracle's router step gives the GPU's own ids.  Returns those
+    oracle weights (float64 [T, k]) for the output reference."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    lf = np.asarray(r["logits_f32"], dtype=np.float64)
+    E = lf.shape[1]
+    ok = r["margin"] > MARGIN
+    assert np.array_equal(ids[ok], r["topk_ids"][ok]), "routing ids differ on margin tokens"
+    assert np.all((ids >= 0) & (ids < E)), "expert id out of range"
+    assert all(len(set(row)) == k for row in ids.tolist()), "repeated expert id"
+    chosen = np.take_along_axis(lf, ids.astype(np.int64), axis=1)
+    kth = -np.sort(-lf, axis=1)[:, k - 1]
+    assert np.all(chosen >= kth[:, None] - 2 * MARGIN), "a chosen expert is not near the top-k"
+    mask = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(mask, ids.astype(np.int64), True, axis=1)
+    clearly_in = lf > chosen.min(axis=1, keepdims=True) + 2 * MARGIN
+    assert not np.any(clearly_in & ~mask), "an expert clearly above the chosen ones was dropped"
+    assert np.all(np.diff(chosen, axis=1) <= 2 * MARGIN), "slots not in descending order"
+    w_ref = mo.weights_of(r["logits"], ids, renormalize)
+    assert np.abs(np.asarray(wts, dtype=np.float64) - w_ref).max() <= WEIGHT_TOL, \
+        "routing weights differ from the oracle's weights of the same experts"
+    return w_ref
+
+
+def scatter_routing(M: int, toks: np.ndarray, ids: np.ndarray, wts: np.ndarray):
+    """[M, k] id and weight arrays holding the sampled tokens' rows."""
+    k = ids.shape[1]
+    full_ids = np.zeros((M, k), dtype=np.int32)
+    full_w = np.zeros((M, k))
+    full_ids[toks] = ids
+    full_w[toks] = wts
+    return full_ids, full_w

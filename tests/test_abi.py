@@ -216,3 +216,28 @@ def test_mx_workspace_and_quantize_checks():
     w = moe.MxWeights(*([0x10000] * 4))
     assert lib.moe_forward_mxfp8(fake, fake, NULL, ctypes.byref(w), 4, 128, 8, 2048, 768, 1, fake,
                                  NULL, NULL, fake, 1024, NULL, NULL) == -3
+
+
+def test_forward_list_offsets():
+    """Where moe_forward leaves its index lists: inside the workspace,
+    non-overlapping, at the tile table's block size; no lists for the
+    per-pair batches."""
+    moe = _moe()
+    E, k, H, I = 128, 8, 2048, 768
+    o = moe.moe_forward_list_offsets(1, E, k, H, I)
+    assert o["sorted"] == 0 and o["block_m"] == 1
+    for M in (16, 64, 512, 4096):
+        o = moe.moe_forward_list_offsets(M, E, k, H, I)
+        B = moe.moe_pick_block_m(M, E, k)
+        assert o["sorted"] == 1 and o["block_m"] == B
+        cap, nbl = moe.align_capacity(M * k, E, B)
+        spans = sorted([(o["sorted_token_ids"], 4 * cap), (o["expert_ids"], 4 * nbl),
+                        (o["expert_block_offsets"], 4 * (E + 1)), (o["expert_counts"], 4 * E)])
+        for (a, n), (b, _) in zip(spans, spans[1:]):
+            assert a + n <= b
+        assert spans[-1][0] + spans[-1][1] <= moe.moe_workspace_size(M, E, k, H, I)
+        assert all(off % 16 == 0 for off, _ in spans)
+    import ctypes
+    assert moe.library().moe_forward_list_offsets(4, E, k, H, I, None) == -1
+    lists = moe.ForwardLists()
+    assert moe.library().moe_forward_list_offsets(4, E, 0, H, I, ctypes.byref(lists)) == -1

@@ -2,9 +2,12 @@
 every workload shape, plus the layer's special cases and robustness checks.
 
 Routing ids are compared bit-exactly on tokens whose top-k logit margin
-exceeds 1e-4; outputs are compared on those tokens with the max-abs and
-mean-relative criteria.  At the large batch sizes the oracle checks a seeded
-sample of tokens (it computes them one expert group at a time)."""
+exceeds 1e-4 and checked for validity on the others; the outputs of every
+sampled token are compared, with the max-abs and mean-relative criteria,
+against the oracle's expert layer run on the GPU's own ids with the oracle's
+weights for those ids (so near-tie tokens are checked too).  At the large
+batch sizes the oracle checks a seeded sample of tokens (it computes them one
+expert group at a time)."""
 
 from __future__ import annotations
 
@@ -41,14 +44,13 @@ def check_forward(lay: dict, n_tokens: int = 256, seed: int = 0, **kw):
     out, ids, wts, info = run_forward(lay, **kw)
     M = lay["M"]
     toks = h.sample_tokens(M, n_tokens, seed)
-    ref = mo.forward(lay, tokens=toks)
-    r = ref["route"]
-    ok = r["margin"] > h.MARGIN
-    assert ok.mean() >= 0.9
-    assert np.array_equal(ids[toks][ok], r["topk_ids"][ok])
-    assert np.abs(wts[toks][ok] - r["topk_weights"][ok]).max() <= h.WEIGHT_TOL
+    r = mo.route(lay["x"][toks], lay["w_router"], lay["top_k"], lay["renormalize"],
+                 lay.get("logit_bias"))
+    w_ref = h.check_routing(ids[toks], wts[toks], r, lay["renormalize"])
+    full_ids, full_w = h.scatter_routing(M, toks, ids[toks], w_ref)
+    ref_y = mo.layer_forward(lay["x"], lay["w13"], lay["w2"], full_ids, full_w, toks)
     y = h.host_bf16_to_f64(out)[toks]
-    h.assert_close_outputs(y[ok], ref["y"][ok])
+    h.assert_close_outputs(y, ref_y)
     return info, out
 
 

@@ -231,3 +231,37 @@ def test_route_deterministic():
     b = run_route(lay)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# the index lists moe_forward builds from its own routing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [16, 64, 256, 512])
+def test_forward_index_lists_bit_exact(M):
+    """The lists moe_forward leaves in its workspace equal oracle.align of
+    the GPU's own topk_ids, bit for bit: the fused top-k + index-list launch
+    with one workgroup (16 tokens), several (64), the most a one-segment
+    batch takes (256 tokens = 2048 pairs), and the two-kernel align of a
+    multi-segment batch (512)."""
+    import torch
+    moe = _moe()
+    lay = wl.make_layer("qwen3_decode", M)
+    M, E, k, H, I = lay["M"], lay["E"], lay["top_k"], lay["H"], lay["I"]
+    d = h.layer_to_device(lay)
+    ws = moe.workspace(M, E, k, H, I)
+    ws.fill_(0xFF)
+    ids = torch.full((M, k), -1, dtype=torch.int32, device="cuda")
+    print(f"index lists case M={M}", flush=True)
+    _, info = moe.moe_forward(d["x"], d["w_router"], d["w13"], d["w2"], k, True,
+                              topk_ids_out=ids, ws=ws)
+    torch.cuda.synchronize()
+    s, e, off, cnt, B = moe.forward_lists(ws, M, E, k, H, I)
+    assert B == info["block_m"]
+    ref = mo.align(ids.cpu().numpy(), E, B)
+    off = off.cpu().numpy()
+    nb = int(off[E])
+    assert np.array_equal(off, ref["expert_block_offsets"])
+    assert np.array_equal(cnt.cpu().numpy(), ref["expert_counts"])
+    assert np.array_equal(e.cpu().numpy()[:nb], ref["expert_ids"])
+    assert np.array_equal(s.cpu().numpy()[:nb * B], ref["sorted_token_ids"])

@@ -202,6 +202,74 @@ def test_toy_workload_matches_bruteforce():
     assert np.allclose(o["y"], y_b, rtol=1e-10, atol=1e-12)
 
 
+# Teacher-forced halves of the layer (what the per-step GEMM tests compare
+# against): the activation rows of every pair in pair order, the output from
+# given activation rows, and the router weights of given (not necessarily
+# top-k) experts, each against the brute force on random routings that
+# repeat experts across tokens and need not be any router's top-k.
+
+TF_CASES = [
+    dict(seed=31, M=4, E=5, top_k=3, H=8, I=4),
+    dict(seed=32, M=3, E=3, top_k=2, H=12, I=6, bias=True),
+    dict(seed=33, M=5, E=7, top_k=1, H=6, I=3),
+]
+
+
+def _random_ids(M, E, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+
+
+def check_pair_activations_bruteforce(case):
+    lay = tiny_layer(**case)
+    X, _, W13, _ = bf.to_lists(lay)
+    ids = _random_ids(lay["M"], lay["E"], lay["top_k"], case["seed"])
+    want = np.asarray(bf.pair_rows(X, W13, ids.tolist()))
+    got = mo.pair_activations(lay["x"], lay["w13"], ids)
+    assert got.shape == want.shape
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def check_combine_from_act_bruteforce(case):
+    lay = tiny_layer(**case)
+    _, _, _, W2 = bf.to_lists(lay)
+    M, k, I = lay["M"], lay["top_k"], lay["I"]
+    ids = _random_ids(M, lay["E"], k, case["seed"] + 1)
+    rng = np.random.default_rng(case["seed"])
+    act = wl.f32_to_bf16_bits(rng.standard_normal((M * k, I)).astype(np.float32))
+    wts = rng.uniform(0.05, 1.0, (M, k))
+    A = [[bf.bf16_to_float(v) for v in row] for row in act]
+    want = np.asarray(bf.combine(A, W2, ids.tolist(), wts.tolist()))
+    got = mo.combine_from_act(act, lay["w2"], ids, wts)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def check_weights_of_bruteforce(case):
+    lay = tiny_layer(**case)
+    X, WR, _, _ = bf.to_lists(lay)
+    ids = _random_ids(lay["M"], lay["E"], lay["top_k"], case["seed"] + 2)
+    bias = lay.get("logit_bias")
+    logits = mo.router_logits(lay["x"], lay["w_router"], bias)
+    for renorm in (True, False):
+        want = [bf.weights_of_ids(xv, WR, row, renorm, bias) for xv, row in zip(X, ids.tolist())]
+        assert np.allclose(mo.weights_of(logits, ids, renorm), want, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("case", TF_CASES, ids=lambda c: f"seed{c['seed']}")
+def test_pair_activations_match_bruteforce(case):
+    check_pair_activations_bruteforce(case)
+
+
+@pytest.mark.parametrize("case", TF_CASES, ids=lambda c: f"seed{c['seed']}")
+def test_combine_from_act_matches_bruteforce(case):
+    check_combine_from_act_bruteforce(case)
+
+
+@pytest.mark.parametrize("case", TF_CASES, ids=lambda c: f"seed{c['seed']}")
+def test_weights_of_given_ids_match_bruteforce(case):
+    check_weights_of_bruteforce(case)
+
+
 # ---------------------------------------------------------------------------
 # library special cases
 # ---------------------------------------------------------------------------
@@ -347,6 +415,9 @@ def _battery():
     checks = [check_page_toy, check_swiglu_hand, check_route_hand, check_combine_hand,
               check_ties]
     checks += [lambda c=c: check_against_bruteforce(c) for c in BF_CASES]
+    checks += [lambda c=c, f=f: f(c) for c in TF_CASES
+               for f in (check_pair_activations_bruteforce, check_combine_from_act_bruteforce,
+                         check_weights_of_bruteforce)]
     checks += [lambda: check_align_invariants(
         wl.make_topk_ids(37, 4, 60, seed=5, pattern="random"), 60, 4)]
     for c in checks:
@@ -447,6 +518,47 @@ def _expert_w2_transposed(x_rows, w13_e, w2_e, return_act=False):
     return (y, a) if return_act else y
 
 
+def _pair_activations_slot_major(x, w13, topk_ids, tokens=None):
+    M, k = topk_ids.shape
+    I = w13.shape[1] // 2
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    X = mo.widen_bf16(x)
+    act = np.full((M * k, I), np.nan)
+    for e, ts, js in _orig_pairs(topk_ids, tokens):
+        act[js * M + ts] = mo.swiglu(X[ts] @ mo.widen_bf16(w13[e]).T, I)   # wrong row
+    return act
+
+
+def _combine_rows_slot_major(act_bits, w2, topk_ids, topk_weights, tokens=None):
+    M, k = topk_ids.shape
+    H = w2.shape[1]
+    tokens = np.arange(M) if tokens is None else np.asarray(tokens)
+    pos = np.full(M, -1)
+    pos[tokens] = np.arange(tokens.size)
+    A = mo.widen_bf16(act_bits)
+    slots = np.zeros((tokens.size, k, H))
+    for e, ts, js in _orig_pairs(topk_ids, tokens):
+        slots[pos[ts], js] = A[js * M + ts] @ mo.widen_bf16(w2[e]).T   # wrong row
+    return np.einsum("tk,tkh->th", np.asarray(topk_weights, np.float64)[tokens], slots)
+
+
+_orig_combine = mo.combine_from_act
+
+
+def _combine_weight_of_next_slot(act_bits, w2, topk_ids, topk_weights, tokens=None):
+    w = np.roll(np.asarray(topk_weights, np.float64), 1, axis=1)
+    return _orig_combine(act_bits, w2, topk_ids, w, tokens)
+
+
+_orig_weights_of = mo.weights_of
+
+
+def _weights_softmax_over_kept_only(logits, ids, renormalize):
+    kept = np.take_along_axis(np.asarray(logits, np.float64), np.asarray(ids, np.int64), axis=1)
+    ex = np.exp(kept - kept.max(axis=1, keepdims=True))
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
 MUTANTS = {
     "swap_gate_up": ("swiglu", _swap_gate_up),
     "silu_wrong_sign": ("swiglu", _silu_wrong_sign),
@@ -461,6 +573,10 @@ MUTANTS = {
     "router_rows_permuted": ("router_logits", _logits_transposed_weights),
     "combine_wrong_slot_weight": ("_pairs_by_expert", _pairs_wrong_slot),
     "w2_wrong_layout": ("expert_ffn", _expert_w2_transposed),
+    "pair_rows_slot_major": ("pair_activations", _pair_activations_slot_major),
+    "combine_reads_slot_major_rows": ("combine_from_act", _combine_rows_slot_major),
+    "combine_weight_of_next_slot": ("combine_from_act", _combine_weight_of_next_slot),
+    "softmax_over_kept_experts_only": ("weights_of", _weights_softmax_over_kept_only),
 }
 
 

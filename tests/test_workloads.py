@@ -53,3 +53,19 @@ def test_zipf_prefill_router_has_empty_experts():
     assert counts.max() > 0.5 * 4096
     rank = np.round(np.exp(-lay["logit_bias"] / 1.1)).astype(int)
     assert sorted(rank.tolist()) == list(range(1, s.E + 1))
+
+
+def test_mx_weights_cover_every_finite_e4m3_code():
+    """MXFP8 weight codes are uniform over the 254 finite E4M3 codes (zeros,
+    subnormals, exponent fields 1..15, +-448) and never NaN; the weights
+    spread near 1/sqrt(K)."""
+    from oracle import moe_oracle as mo
+    lay = wl.make_mx_layer("toy", 3, E=2, top_k=1, H=512, I=256, seed=5)
+    codes = np.concatenate([lay["w13_codes"].ravel(), lay["w2_codes"].ravel()])
+    present = set(np.unique(codes).tolist())
+    assert present == set(range(256)) - {0x7F, 0xFF}
+    for c in (0x00, 0x80, 0x01, 0x07, 0x08, 0x7E, 0xFE):
+        assert c in present
+    w = mo.mx_dequantize(lay["w13_codes"][0], lay["w13_scales"][0])
+    assert np.all(np.isfinite(w))
+    assert 0.5 < w.std() * np.sqrt(512) < 2.0
