@@ -228,6 +228,30 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* logit_
                 void* workspace, size_t ws_bytes, moe_dispatch_info* info, void* stream);
 
 /*
+ * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same layer, kernels and results, with the
+ * scratch memory in a device array of this library
+ * (MOE_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends) instead of a caller workspace.  The caller still
+ * passes inputs and outputs, as for moe_forward; nothing is allocated,
+ * freed or synchronized.
+ *   - A batch whose moe_workspace_size(M, E, top_k, H, I) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE before any launch
+ *     (Qwen3-30B-A3B shape: up to about 850 tokens).
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's contents (the kernels clear what must start at zero).  Calls
+ *     that overlap on one GPU (other streams, other threads) race on it:
+ *     serialize them, or use moe_forward with separate workspaces.
+ *   - MOE_ERR_HIP if the array's address cannot be looked up.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
+                        const uint16_t* w13, const uint16_t* w2, int M, int E, int top_k, int H,
+                        int I, int renormalize, uint16_t* out, int32_t* topk_ids_out,
+                        float* topk_weights_out, moe_dispatch_info* info, void* stream);
+
+/*
  * Where moe_forward leaves the index lists of a batch in its workspace
  * (host struct): byte offsets from the workspace start, valid after a
  * moe_forward call with the same (M, E, top_k, H, I) on that workspace

@@ -87,6 +87,9 @@ _SIGNATURES = {
     "moe_forward": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
                     [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                      ctypes.POINTER(DispatchInfo), _c_void_p]),
+    "moe_forward_noalloc": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 +
+                            [_c_void_p, _c_void_p, _c_void_p, ctypes.POINTER(DispatchInfo),
+                             _c_void_p]),
     "moe_forward_list_offsets": (_c_int, [_c_int] * 5 + [ctypes.POINTER(ForwardLists)]),
     "moe_mx_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "moe_mx_workspace_size": (_c_size_t, [_c_int] * 5),
@@ -338,6 +341,41 @@ def moe_forward(x, w_router, w13, w2, top_k: int, renormalize: bool = True,
         int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
         _ptr(ws), ws.numel(), ctypes.byref(info), _stream(stream))
     _raise("moe_forward", st)
+    return out, info.as_dict()
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(x, w_router, w13, w2, top_k: int, renormalize: bool = True,
+                        logit_bias=None, out=None, topk_ids_out=None, topk_weights_out=None,
+                        stream=None):
+    """moe_forward with the library's own device scratch array (no workspace
+    argument; allocates no device memory when ``out`` is given).  Returns
+    (out [M, H] bf16, dispatch info dict)."""
+    torch = _torch()
+    M, H = x.shape
+    E, two_i, _ = w13.shape
+    I = two_i // 2
+    _check(x, "x", _bf16_types())
+    _check(w_router, "w_router", _bf16_types(), (E, H))
+    _check(w13, "w13", _bf16_types(), (E, 2 * I, H))
+    _check(w2, "w2", _bf16_types(), (E, H, I))
+    if logit_bias is not None:
+        _check(logit_bias, "logit_bias", (torch.float32,), (E,))
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", _bf16_types(), (M, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", (torch.int32,), (M, top_k))
+    if topk_weights_out is not None:
+        _check(topk_weights_out, "topk_weights_out", (torch.float32,), (M, top_k))
+    info = DispatchInfo()
+    st = library().moe_forward_noalloc(
+        _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w13), _ptr(w2), M, E, top_k, H, I,
+        int(bool(renormalize)), _ptr(out), _ptr(topk_ids_out), _ptr(topk_weights_out),
+        ctypes.byref(info), _stream(stream))
+    _raise("moe_forward_noalloc", st)
     return out, info.as_dict()
 
 
