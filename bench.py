@@ -20,6 +20,7 @@ Prints ONE JSON line:
                    mean launch time against the bf16 MFMA peak)
   mxfp8            context: moe_forward_mxfp8 (MXFP8 experts and GEMM inputs)
                    on the same shape and batch, the L layers drawn as MXFP8
+                   (mxfp8_M1: the same at one token, the per-pair GEMVs)
   quantized        context: moe_forward_quantized (affine 64-element groups,
                    4 and 8 bits) on the same shape at M = 1 and 4, one captured
                    HIP graph of the L layers replayed
@@ -50,7 +51,7 @@ PREFILL_WORKLOAD = ("qwen3_prefill", 4096)
 
 
 VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8",
-                 5: "stream_mxfp8"}
+                 5: "stream_mxfp8", 6: "pair_gemv_mxfp8"}
 
 
 def parse_args():
@@ -262,6 +263,10 @@ def main():
     # ---- MXFP8 experts and GEMM inputs at the same batch (context) ----
     if not args.no_mx and H % 128 == 0 and I % 128 == 0:
         result["mxfp8"] = mxfp8_figures(shape, M, L, x, dev, max(5, min(args.steps, 50)))
+        if M > 1 and name == "qwen3_decode":
+            # one token: the per-pair MXFP8 GEMVs, beside decode_sweep's bf16 M=1
+            result["mxfp8_M1"] = mxfp8_figures(shape, 1, L, x[:1].contiguous(), dev,
+                                               max(5, min(args.steps, 50)))
 
     # ---- group-quantized expert weights at small batches (context) ----
     if not args.no_quant and shape.H % 64 == 0 and shape.I % 64 == 0 and M <= 64:

@@ -72,6 +72,8 @@ typedef enum moe_status {
                                       MXFP8 operands */
 #define MOE_VARIANT_STREAM_MXFP8 5  /* moe_forward_mxfp8: weight-streaming scaled-MFMA
                                        GEMMs on MXFP8 operands (block_m 16) */
+#define MOE_VARIANT_PAIR_GEMV_MXFP8 6  /* moe_forward_mxfp8: per-pair GEMVs on MXFP8
+                                          weights and inputs (M*top_k*4 <= E, no lists) */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -361,15 +363,21 @@ size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I);
  * (E4M3 x E4M3, each 32-element block scaled by its E8M0 factor, fp32
  * accumulation) with SiLU(gate)*up, act stored bf16; act quantized to
  * MXFP8; GEMM 2 likewise into bf16 pair-order rows; the weighted top-k sum
- * per token.  Index lists with block_m = moe_pick_block_m(M, E, top_k), at
- * least 16: weight-streaming kernels at block_m 16 (small batches, also the
- * per-pair case), tiled kernels above.
+ * per token.  Index lists with block_m = moe_pick_block_m(M, E, top_k):
+ * weight-streaming kernels at block_m 16, tiled kernels above.  Very small
+ * batches (M*top_k*4 <= E, page "Mixture of Experts in vLLM ...",
+ * sub-section "Small batches skip the sort") build no lists: the top-k
+ * launch also quantizes x, GEMV 1 runs each pair against its expert's
+ * MXFP8 rows, and GEMV 2 quantizes each act row to MXFP8 in registers and
+ * sums the weighted slots per token (four launches; info->variant
+ * MOE_VARIANT_PAIR_GEMV_MXFP8, info->sorted 0).
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, info,
  *   stream: as for moe_forward;  w: host struct of device pointers
  *   workspace: at least moe_mx_workspace_size(M, ...) bytes, 16-byte aligned
  * H and I must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise).
- * info->variant reads MOE_VARIANT_STREAM_MXFP8 or MOE_VARIANT_TILED_MXFP8.
+ * info->variant reads MOE_VARIANT_PAIR_GEMV_MXFP8, MOE_VARIANT_STREAM_MXFP8 or
+ * MOE_VARIANT_TILED_MXFP8.
  */
 int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
                       const moe_mx_weights* w, int M, int E, int top_k, int H, int I,

@@ -456,12 +456,8 @@ struct MxLayout {
   size_t qx, sx, qact, sact, total;
 };
 
-// the tile table's block size, with the per-pair case on the streaming
-// kernels (block_m 16)
-int mx_block_m(int M, int E, int top_k) {
-  const int B = moe_pick_block_m(M, E, top_k);
-  return B < 16 ? 16 : B;
-}
+// the tile table's block size (1: per-pair MXFP8 GEMVs, no index lists)
+int mx_block_m(int M, int E, int top_k) { return moe_pick_block_m(M, E, top_k); }
 
 MxLayout mx_layout(int M, int E, int top_k, int H, int I, int B) {
   MxLayout L;
@@ -500,7 +496,7 @@ int moe_mx_quantize(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_
 size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I) {
   if (check_sizes(M_max, E, top_k, H, I) != MOE_OK || !mx_sizes_ok(H, I)) return 0;
   size_t best = 0;
-  for (int B : {16, 64, 128, 256}) best = std::max(best, mx_layout(M_max, E, top_k, H, I, B).total);
+  for (int B : kBlockSizes) best = std::max(best, mx_layout(M_max, E, top_k, H, I, B).total);
   return std::max<size_t>(best, kAlign);
 }
 
@@ -515,10 +511,18 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
   if (w == nullptr) return MOE_ERR_INVALID_ARG;
   if (!mx_sizes_ok(H, I)) return MOE_ERR_UNSUPPORTED;
   const int B = mx_block_m(M, E, top_k);
+  const bool per_pair = B == 1;
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
-  // quantize x, GEMM 1, quantize act, then GEMM 2 and its per-token sum
-  fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 3 + kGemm2Launches);
-  if (info != nullptr) info->variant = B == 16 ? MOE_VARIANT_STREAM_MXFP8 : MOE_VARIANT_TILED_MXFP8;
+  if (per_pair) {
+    // router logits, top-k (+ x quantized), GEMV 1, GEMV 2 with the sum
+    fill_info(info, B, H, I, M == 0 ? 0 : kPairGemvForwardLaunches, 0);
+    if (info != nullptr) info->variant = MOE_VARIANT_PAIR_GEMV_MXFP8;
+  } else {
+    // quantize x, GEMM 1, quantize act, then GEMM 2 and its per-token sum
+    fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 3 + kGemm2Launches);
+    if (info != nullptr)
+      info->variant = B == 16 ? MOE_VARIANT_STREAM_MXFP8 : MOE_VARIANT_TILED_MXFP8;
+  }
   if (M == 0) return MOE_OK;
   if (!x || !w_router || !out || !w->w13_codes || !w->w13_scales || !w->w2_codes ||
       !w->w2_scales)
@@ -549,6 +553,18 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
                reinterpret_cast<int32_t*>(ws + L.counts),
                reinterpret_cast<int32_t*>(ws + L.align_scratch)};
   MOE_TRY_HIP(launch_route_logits(ra, s));
+  if (per_pair) {
+    // Small batches skip the sort: the top-k launch also quantizes x, and
+    // each pair runs as its own GEMV against its expert's MXFP8 rows.
+    ra.qx_codes = qx;
+    ra.qx_scales = sx;
+    MOE_TRY_HIP(launch_route_topk(ra, s));
+    MxPairGemvArgs pg{qx, sx, w->w13_codes, w->w13_scales, w->w2_codes, w->w2_scales, ids, wts,
+                      M, top_k, H, I, act, out};
+    MOE_TRY_HIP(launch_mx_pair_gemv1(pg, s));
+    MOE_TRY_HIP(launch_mx_pair_gemv2(pg, s));
+    return MOE_OK;
+  }
   if (fused_route(M, top_k)) {
     MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive), s));
   } else {

@@ -96,6 +96,80 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// ---- MXFP8 (OCP microscaling: E8M0 scale per 32 values, E4M3 elements) ----
+
+// The nearest E4M3 magnitude to a >= 0, ties to the even code, saturated at
+// 448: steps of 2^-9 below 2^-6 (subnormals), 3 mantissa bits above.
+__device__ __forceinline__ float e4m3_round_mag(float a) {
+  const float sub = __builtin_rintf(a * 512.f) * (1.f / 512.f);
+  uint32_t u = __float_as_uint(a);
+  u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;   // drop 20 bits, ties to even
+  const float r = a < 0.015625f ? sub : __uint_as_float(u);
+  return r < 448.f ? r : 448.f;
+}
+
+// E4M3 magnitude code (7 bits) of an exactly representable magnitude r.
+__device__ __forceinline__ uint32_t e4m3_code_of_mag(float r) {
+  if (r < 0.015625f) return (uint32_t)(r * 512.f);        // subnormal codes 0..7
+  const uint32_t u = __float_as_uint(r);
+  return ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+// Shared exponent of a block whose largest magnitude is amax: floor(log2
+// amax) - 8 (8 = the exponent of E4M3's largest power of two), clamped to
+// E8M0's range [-127, 127]; -127 for a zero or subnormal amax.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  const int s = ef == 0 ? -127 : ef - 127 - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// E4M3 byte of v * 2^-shared (nearest, ties to even, saturated, sign kept).
+__device__ __forceinline__ uint32_t e4m3_of(float v, int shared) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  return sign | e4m3_code_of_mag(e4m3_round_mag(__builtin_ldexpf(__builtin_fabsf(v), -shared)));
+}
+
+// Block b (32 values) of the bf16 rows src [rows, K] into E4M3 codes and its
+// E8M0 scale byte (K % 32 == 0; src and codes 16-byte aligned).
+__device__ __forceinline__ void mx_quantize_block(const uint16_t* __restrict__ src, int K,
+                                                  long long b, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales) {
+  const int nb = K / 32;
+  const long long row = b / nb;
+  const int blk = (int)(b - row * nb);
+  const size_t base = (size_t)row * K + (size_t)blk * 32;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src + base);
+  u32x4 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = s4[i];
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = bf16_lo(w[i][j]);
+      v[8 * i + 2 * j + 1] = bf16_hi(w[i][j]);
+    }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  const int shared = mx_shared_exp(amax);
+  u32x4 out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i0 = 16 * h + 4 * j;
+      out[h][j] = e4m3_of(v[i0], shared) | (e4m3_of(v[i0 + 1], shared) << 8) |
+                  (e4m3_of(v[i0 + 2], shared) << 16) | (e4m3_of(v[i0 + 3], shared) << 24);
+    }
+  u32x4* d4 = reinterpret_cast<u32x4*>(codes + base);
+  d4[0] = out[0];
+  d4[1] = out[1];
+  scales[b] = (uint8_t)(shared + 127);
+}
+
 // Wave-wide reductions over 64 lanes.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -310,6 +384,8 @@ struct RouteArgs {
   float* topk_weights;  // [M, top_k]
   float* zero_ptr;      // optional region to clear (arrival counter of the fused top-k + align)
   size_t zero_words;    // number of 4-byte words to clear
+  uint8_t* qx_codes;    // optional: launch_route_topk also writes MXFP8 codes [M, H] of x
+  uint8_t* qx_scales;   //           and their E8M0 scales [M, H/32] (H % 32 == 0)
 };
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s);
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s);
@@ -394,6 +470,26 @@ struct QPairGemvArgs {
   uint16_t* act;                // [M*top_k, I]
   uint16_t* out;                // [M, H]
 };
+// Per-pair GEMVs on MXFP8 expert weights: GEMV 1 reads the MXFP8 codes of x
+// (written by the top-k launch) and writes act [P, I] bf16; GEMV 2 quantizes
+// each act row to MXFP8 in registers, multiplies, weights and sums each
+// token's top_k rows into out [M, H].  H, I multiples of 128.
+struct MxPairGemvArgs {
+  const uint8_t* qx;            // [M, H] E4M3
+  const uint8_t* qx_scales;     // [M, H/32] E8M0
+  const uint8_t* w13;           // [E, 2I, H] E4M3
+  const uint8_t* w13_scales;    // [E, 2I, H/32]
+  const uint8_t* w2;            // [E, H, I] E4M3
+  const uint8_t* w2_scales;     // [E, H, I/32]
+  const int32_t* topk_ids;      // [M, top_k]
+  const float* topk_weights;    // [M, top_k]
+  int M, top_k, H, I;
+  uint16_t* act;                // [M*top_k, I]
+  uint16_t* out;                // [M, H]
+};
+hipError_t launch_mx_pair_gemv1(const MxPairGemvArgs& a, hipStream_t s);
+hipError_t launch_mx_pair_gemv2(const MxPairGemvArgs& a, hipStream_t s);
+
 hipError_t launch_qpair_gemv1(const QPairGemvArgs& a, hipStream_t s);
 hipError_t launch_qpair_gemv2(const QPairGemvArgs& a, hipStream_t s);
 

@@ -249,11 +249,22 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
   }
 }
 
-// Softmax over all E, ordered top-k, renormalize; one wave per token.
+// Softmax over all E, ordered top-k, renormalize; one wave per token.  With
+// qx non-null the workgroup also writes the MXFP8 codes and scales of its
+// four tokens' x rows (the quantized GEMM 1 input of the MXFP8 layer, page
+// "Mixture of Experts in vLLM ...", sub-section "The two index lists":
+// qhidden), so that no separate launch is needed.
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int M, int E, int top_k, int renormalize,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ qx, uint8_t* __restrict__ qxs) {
   __shared__ __attribute__((aligned(16))) float scratch[4][topk_wave_floats(512)];
+  if (qx != nullptr) {
+    const long long nb = H / 32;
+    const long long b0 = (long long)blockIdx.x * 4 * nb;
+    const long long b1 = (long long)min(M, (int)blockIdx.x * 4 + 4) * nb;
+    for (long long b = b0 + threadIdx.x; b < b1; b += 256) mx_quantize_block(x, H, b, qx, qxs);
+  }
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
   if (t >= M) return;   // whole wave; no workgroup barrier below
@@ -336,7 +347,8 @@ hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div_host(a.M, 4));
   hipLaunchKernelGGL(route_topk_kernel, grid, dim3(256), 0, s, a.logits, a.M, a.E, a.top_k,
-                     a.renormalize, a.topk_ids, a.topk_weights);
+                     a.renormalize, a.topk_ids, a.topk_weights, a.x, a.H, a.qx_codes,
+                     a.qx_scales);
   return hipGetLastError();
 }
 

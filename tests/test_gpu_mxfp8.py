@@ -10,7 +10,9 @@ oracle's mx_quantize and forward_mxfp8.
   elsewhere), weights to 1e-5, outputs within 2e-2 max-abs (relative to max |ref|) and 5e-3
   mean-relative, through the weight-streaming kernels (block_m 16: small
   layers, the Qwen3-30B-A3B decode shape at 1, 8 and 64 tokens, the
-  Qwen1.5-MoE shape whose I = 1408 leaves a ragged last slice, 256 experts)
+  Qwen1.5-MoE shape whose I = 1408 leaves a ragged last slice, 256 experts),
+  the per-pair MXFP8 GEMVs of very small batches (no index lists; x
+  quantized by the top-k launch, act quantized in registers by GEMV 2)
   and the tiled kernels (a mid layer, the Qwen1.5-MoE shape at 512 and 2048
   tokens, the Qwen3 prefill shape with its Zipf prior at block_m 128), plus
   a poisoned workspace; weight codes span the whole finite E4M3 range.
@@ -111,14 +113,20 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
     print(f"mxfp8 case {lay['name']} M={lay['M']} E={lay['E']} k={lay['top_k']} "
           f"H={lay['H']} I={lay['I']}", flush=True)
     out, ids, wts, info = run_mx(lay, **kw)
-    B = max(16, moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"]))
+    B = moe.moe_pick_block_m(lay["M"], lay["E"], lay["top_k"])
     assert info["block_m"] == B
-    # router logits, top-k + lists (one launch, or top-k, count, scatter),
-    # quantize x, GEMM 1, quantize act, GEMM 2, per-token sum
     P = lay["M"] * lay["top_k"]
-    route_launches = 2 if P <= 2048 else 4
-    assert info["launches"] == route_launches + 5
-    assert info["variant"] == (moe.MOE_VARIANT_STREAM_MXFP8 if B == 16 else moe.MOE_VARIANT_TILED_MXFP8)
+    if P * 4 <= lay["E"]:
+        # router logits, top-k (+ x quantized), GEMV 1, GEMV 2 with the sum
+        assert B == 1 and info["sorted"] == 0 and info["launches"] == 4
+        assert info["variant"] == moe.MOE_VARIANT_PAIR_GEMV_MXFP8
+    else:
+        # router logits, top-k + lists (one launch, or top-k, count, scatter),
+        # quantize x, GEMM 1, quantize act, GEMM 2, per-token sum
+        route_launches = 2 if P <= 2048 else 4
+        assert info["launches"] == route_launches + 5 and info["sorted"] == 1
+        assert info["variant"] == (moe.MOE_VARIANT_STREAM_MXFP8 if B == 16
+                                   else moe.MOE_VARIANT_TILED_MXFP8)
     toks = h.sample_tokens(lay["M"], n_tokens, seed)
     r = mo.route(lay["x"][toks], lay["w_router"], lay["top_k"], lay["renormalize"],
                  lay.get("logit_bias"))
@@ -130,14 +138,24 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
     return out
 
 
-# block_m 16 (streaming): toy M=5, Qwen3 decode M=1, 8 and 64, Qwen1.5 M=16
+# per-pair MXFP8 GEMVs (M*top_k*4 <= E): a small layer, H = 4224 (two
+# passes of GEMV 1, the second ragged) with I = 1408 (a ragged GEMV 2 pass),
+# top_k = 12 (more slots than GEMV 2's eight waves), the Qwen3 decode shape
+# at 1, 2 and 4 tokens, the Qwen1.5 shape at 1 token, 256 experts at 8;
+# block_m 16 (streaming): toy M=5, Qwen3 decode M=8 and 64, Qwen1.5 M=16
 # (I = 1408: a ragged last slice in both streaming kernels), 256 experts
 # M=8; tiled: toy M=70, Qwen1.5 M=512 (block_m 64), toy M=300 (block_m 128,
 # the copy-wave tiles), Qwen1.5 M=2048 (136 pairs per expert: block_m 256,
 # the eight-wave tiles with a two-stage ring), Qwen3 prefill (block_m 128).
 # Weight codes are uniform over every finite E4M3 code (zeros, subnormals,
 # all exponent fields, +-448).
-MX_CASES = [("toy", 5, dict(E=8, top_k=2, H=256, I=128)),
+MX_CASES = [("toy", 3, dict(E=64, top_k=2, H=256, I=128)),
+            ("toy", 2, dict(E=64, top_k=2, H=4224, I=1408)),
+            ("toy", 2, dict(E=128, top_k=12, H=384, I=256)),
+            ("qwen3_decode", 2, {}),
+            ("qwen3_decode", 4, {}),
+            ("qwen15", 1, {}),
+            ("toy", 5, dict(E=8, top_k=2, H=256, I=128)),
             ("toy", 70, dict(E=6, top_k=2, H=384, I=256)),
             ("toy", 300, dict(E=6, top_k=2, H=384, I=256)),
             ("qwen3_decode", 1, {}),
