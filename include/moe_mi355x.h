@@ -359,7 +359,8 @@ size_t moe_mx_workspace_size(int M_max, int E, int top_k, int H, int I);
 /*
  * moe_forward_mxfp8 -- the layer of moe_forward with MXFP8 expert weights
  * and MXFP8 GEMM inputs: routing on the bf16 router as moe_forward; x
- * quantized to MXFP8 (moe_mx_quantize); GEMM 1 on the gfx950 scaled MFMA
+ * quantized to MXFP8 as moe_mx_quantize does (by the top-k launch); GEMM 1
+ * on the gfx950 scaled MFMA
  * (E4M3 x E4M3, each 32-element block scaled by its E8M0 factor, fp32
  * accumulation) with SiLU(gate)*up, act stored bf16; act quantized to
  * MXFP8; GEMM 2 likewise into bf16 pair-order rows; the weighted top-k sum

@@ -216,16 +216,27 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
 // stores, waits for them, and counts its arrival in *arrivals (zeroed by the
 // router-logits kernel on the same stream) with an agent-scope
 // acquire-release add; the last one reads all P ids back with
-// agent-coherent loads.  A lone workgroup keeps its ids in LDS.
+// agent-coherent loads.  A lone workgroup keeps its ids in LDS.  With qx
+// set, each workgroup also writes the MXFP8 codes of its tokens' x rows.
 __global__ __launch_bounds__(kThreads) void route_topk_align_kernel(
     const float* __restrict__ logits, int M, int E, int top_k, int renormalize, int B,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
     int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
     int32_t* __restrict__ boff_out, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ arrivals) {
+    int32_t* __restrict__ arrivals, const uint16_t* __restrict__ x, int H,
+    uint8_t* __restrict__ qx, uint8_t* __restrict__ qxs) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int s_last;
   const int P = M * top_k;
+  if (qx != nullptr) {
+    // the MXFP8 layer's GEMM 1 input: codes and scales of this workgroup's
+    // tokens' x rows (page "Mixture of Experts in vLLM ...", sub-section
+    // "The two index lists": qhidden)
+    const long long nb = H / 32;
+    const long long b0 = (long long)blockIdx.x * kTopkWaves * nb;
+    const long long b1 = (long long)min(M, ((int)blockIdx.x + 1) * kTopkWaves) * nb;
+    for (long long b = b0 + threadIdx.x; b < b1; b += kThreads) mx_quantize_block(x, H, b, qx, qxs);
+  }
   int* ids_lds = smem + align_smem_ints(E);
   float* tk = reinterpret_cast<float*>(smem + ((align_smem_ints(E) + P + 3) & ~3));
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -281,7 +292,7 @@ hipError_t launch_route_topk_align(const RouteArgs& r, const AlignArgs& a, int32
   hipLaunchKernelGGL(route_topk_align_kernel, dim3(ceil_div_host(r.M, kTopkWaves)), dim3(kThreads),
                      lds, s, r.logits, r.M, r.E, r.top_k, r.renormalize, a.block_m, r.topk_ids,
                      r.topk_weights, a.sorted_token_ids, a.expert_ids, a.expert_block_offsets,
-                     a.expert_counts, arrivals);
+                     a.expert_counts, arrivals, r.x, r.H, r.qx_codes, r.qx_scales);
   return hipGetLastError();
 }
 

@@ -518,8 +518,9 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
     fill_info(info, B, H, I, M == 0 ? 0 : kPairGemvForwardLaunches, 0);
     if (info != nullptr) info->variant = MOE_VARIANT_PAIR_GEMV_MXFP8;
   } else {
-    // quantize x, GEMM 1, quantize act, then GEMM 2 and its per-token sum
-    fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 3 + kGemm2Launches);
+    // GEMM 1, quantize act, then GEMM 2 and its per-token sum (x is
+    // quantized by the top-k launch)
+    fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 2 + kGemm2Launches);
     if (info != nullptr)
       info->variant = B == 16 ? MOE_VARIANT_STREAM_MXFP8 : MOE_VARIANT_TILED_MXFP8;
   }
@@ -565,13 +566,15 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
     MOE_TRY_HIP(launch_mx_pair_gemv2(pg, s));
     return MOE_OK;
   }
+  // the top-k launch also quantizes x
+  ra.qx_codes = qx;
+  ra.qx_scales = sx;
   if (fused_route(M, top_k)) {
     MOE_TRY_HIP(launch_route_topk_align(ra, aa, reinterpret_cast<int32_t*>(ws + L.arrive), s));
   } else {
     MOE_TRY_HIP(launch_route_topk(ra, s));
     MOE_TRY_HIP(launch_align(aa, s));
   }
-  MOE_TRY_HIP(launch_mx_quantize(x, M, H, qx, sx, s));
   GemmArgs g = gemm_args(M, top_k, E, H, I, B);
   g.sorted_token_ids = sorted;
   g.expert_ids = eids;

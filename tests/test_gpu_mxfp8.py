@@ -121,10 +121,10 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
         assert B == 1 and info["sorted"] == 0 and info["launches"] == 4
         assert info["variant"] == moe.MOE_VARIANT_PAIR_GEMV_MXFP8
     else:
-        # router logits, top-k + lists (one launch, or top-k, count, scatter),
-        # quantize x, GEMM 1, quantize act, GEMM 2, per-token sum
+        # router logits, top-k + lists + x quantized (one launch, or top-k
+        # with x, count, scatter), GEMM 1, quantize act, GEMM 2, per-token sum
         route_launches = 2 if P <= 2048 else 4
-        assert info["launches"] == route_launches + 5 and info["sorted"] == 1
+        assert info["launches"] == route_launches + 4 and info["sorted"] == 1
         assert info["variant"] == (moe.MOE_VARIANT_STREAM_MXFP8 if B == 16
                                    else moe.MOE_VARIANT_TILED_MXFP8)
     toks = h.sample_tokens(lay["M"], n_tokens, seed)
