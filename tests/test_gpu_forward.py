@@ -130,6 +130,27 @@ def test_forward_exact_ties_across_lane_blocks(M):
     assert np.abs(wts[ok] - ref["topk_weights"][ok]).max() <= h.WEIGHT_TOL
 
 
+def test_forward_exact_ties_in_pair_gemv():
+    """Ties through the per-pair path (router, top-k launch, GEMVs reading
+    the top-k ids directly)."""
+    from tests.test_gpu_route_align import check_tied_order, tie_layer
+    lay = tie_layer(4)
+    out, ids, wts, info = run_forward(lay)
+    assert info["variant"] == _moe().MOE_VARIANT_PAIR_GEMV
+    ref = mo.route(lay["x"], lay["w_router"], lay["top_k"], True, None)
+    assert check_tied_order(ids, ref["topk_ids"]) >= 2
+    w_ref = h.check_routing(ids, wts, ref, True)
+    y_ref = mo.layer_forward(lay["x"], lay["w13"], lay["w2"], ids, w_ref)
+    h.assert_close_outputs(h.host_bf16_to_f64(out), y_ref)
+
+
+def test_forward_pair_gemv_renormalize_off():
+    lay = wl.make_layer("toy", 2, E=64, top_k=4, H=256, I=128, seed=26)
+    lay["renormalize"] = False
+    info, _ = check_forward(lay)
+    assert info["variant"] == _moe().MOE_VARIANT_PAIR_GEMV
+
+
 def test_forward_all_logits_equal():
     """Zero router: every token keeps experts 0..k-1 with weight 1/k, so the
     layer equals the mean of those experts' FFNs."""
