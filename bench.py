@@ -22,8 +22,9 @@ Prints ONE JSON line:
                    on the same shape and batch, the L layers drawn as MXFP8
                    (mxfp8_M1: the same at one token, the per-pair GEMVs)
   quantized        context: moe_forward_quantized (affine 64-element groups,
-                   4 and 8 bits) on the same shape at M = 1 and 4, one captured
-                   HIP graph of the L layers replayed
+                   4 and 8 bits) on the same shape at M = 1, 4 (per-pair GEMVs)
+                   and 64 (streaming GEMMs), one captured HIP graph of the L
+                   layers replayed
 Default workload: the Qwen3-30B-A3B-shaped decode layer (E=128, top_k=8,
 H=2048, I=768) at M=64 tokens.
 """
@@ -51,7 +52,7 @@ PREFILL_WORKLOAD = ("qwen3_prefill", 4096)
 
 
 VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8",
-                 5: "stream_mxfp8", 6: "pair_gemv_mxfp8"}
+                 5: "stream_mxfp8", 6: "pair_gemv_mxfp8", 7: "stream_quant"}
 
 
 def parse_args():
@@ -67,9 +68,9 @@ def parse_args():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the many-layer stack (eager and HIP-graph replay) figures")
     ap.add_argument("--no-quant", action="store_true",
-                    help="skip the group-quantized (4- and 8-bit) small-batch figures")
-    ap.add_argument("--quant-sizes", default="4:1,4:4,8:1,8:4",
-                    help="bits:M pairs of the quantized figures (default 4:1,4:4,8:1,8:4)")
+                    help="skip the group-quantized (4- and 8-bit) figures")
+    ap.add_argument("--quant-sizes", default="4:1,4:4,4:64,8:1,8:4,8:64",
+                    help="bits:M pairs of the quantized figures (default 4:1,4:4,4:64,8:1,8:4,8:64)")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the MXFP8 figures")
     ap.add_argument("--no-prefill", action="store_true",

@@ -74,6 +74,8 @@ typedef enum moe_status {
                                        GEMMs on MXFP8 operands (block_m 16) */
 #define MOE_VARIANT_PAIR_GEMV_MXFP8 6  /* moe_forward_mxfp8: per-pair GEMVs on MXFP8
                                           weights and inputs (M*top_k*4 <= E, no lists) */
+#define MOE_VARIANT_STREAM_QUANT 7  /* moe_forward_quantized: weight-streaming MFMA
+                                       GEMMs on group-quantized weights (block_m 16) */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -301,20 +303,28 @@ typedef struct moe_quantized_weights {
 
 /*
  * moe_forward_quantized -- the layer of moe_forward with group-quantized
- * expert weights (the router stays bf16).  Every pair runs as its own GEMV
- * against its expert's dequantized rows (page "Mixture of Experts in vLLM
- * ...", sub-section "Small batches skip the sort"; no index lists), the
- * group's scale and bias applied per 16-byte unit of codes; GEMV 2 adds the
- * weighted top_k rows per token in one launch.  Each pair reads its
- * expert's whole weights, so this suits small batches (it is correct for
- * any M).  Four launches: router logits, top-k, GEMV 1, GEMV 2.
+ * expert weights (the router stays bf16).  Up to E/2 pairs
+ * (M*top_k*2 <= E), every pair runs as its own GEMV against
+ * its expert's dequantized rows (page "Mixture of Experts in vLLM ...",
+ * sub-section "Small batches skip the sort"; no index lists), the group's
+ * scale and bias applied per 16-byte unit of codes; GEMV 2 adds the
+ * weighted top_k rows per token in one launch (four launches: router
+ * logits, top-k, GEMV 1, GEMV 2; info->variant MOE_VARIANT_PAIR_GEMV_QUANT,
+ * info->sorted 0).  Larger batches build index lists with block_m 16 (the
+ * same route and align launches as moe_forward) and run weight-streaming
+ * MFMA GEMMs that read each expert's codes once per block: within a
+ * 64-element group, sum w x = s * sum q x + b * sum x, with the codes
+ * widened exactly to bf16 MFMA operands and the scale and bias applied in
+ * fp32 per group; GEMM 2 writes fp32 weighted pair-order rows and a second
+ * kernel sums them per token (info->variant MOE_VARIANT_STREAM_QUANT,
+ * info->sorted 1).  The streaming kernels need H and I to be multiples of
+ * 128; other shapes run the per-pair GEMVs at every M.
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, workspace:
  *                as for moe_forward (same workspace size)
  *   qw           host struct of device pointers, all 16-byte aligned
  * H and I must be multiples of 64 (MOE_ERR_UNSUPPORTED otherwise); a K that
  * is not a multiple of the kernels' 256- or 512-element passes is fine.
- * info->variant reads MOE_VARIANT_PAIR_GEMV_QUANT.
  */
 int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const float* logit_bias,
                           const moe_quantized_weights* qw, int M, int E, int top_k, int H, int I,

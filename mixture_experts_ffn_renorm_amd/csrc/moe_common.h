@@ -493,6 +493,31 @@ hipError_t launch_mx_pair_gemv2(const MxPairGemvArgs& a, hipStream_t s);
 hipError_t launch_qpair_gemv1(const QPairGemvArgs& a, hipStream_t s);
 hipError_t launch_qpair_gemv2(const QPairGemvArgs& a, hipStream_t s);
 
+// Weight-streaming grouped GEMMs on group-quantized experts over index lists
+// with block_m 16: GEMM 1 writes act [P, I]; GEMM 2 writes fp32 weighted
+// pair-order rows into partial [P, H] and its per-token sum into out.
+struct QGemmArgs {
+  const uint16_t* x;            // [M, H]
+  const uint32_t* w13q;         // [E, 2I, H*bits/32]
+  const uint16_t* w13_scales;   // [E, 2I, H/64]
+  const uint16_t* w13_biases;
+  const uint32_t* w2q;          // [E, H, I*bits/32]
+  const uint16_t* w2_scales;    // [E, H, I/64]
+  const uint16_t* w2_biases;
+  const int32_t* sorted_token_ids;
+  const int32_t* expert_ids;
+  const int32_t* expert_block_offsets;
+  const float* topk_weights;    // [M*top_k]
+  int M, top_k, E, H, I, bits, max_blocks;
+  uint16_t* act;                // [M*top_k, I]
+  float* partial;               // [M*top_k, H]
+  uint16_t* out;                // [M, H]
+};
+// H and I multiples of 128
+bool qgemm_stream_shapes_ok(int H, int I);
+hipError_t launch_qgemm1_stream(const QGemmArgs& a, hipStream_t s);
+hipError_t launch_qgemm2_stream(const QGemmArgs& a, hipStream_t s);
+
 hipError_t launch_pair_gemv1(const PairGemvArgs& a, hipStream_t s);
 hipError_t launch_pair_gemv2(const PairGemvArgs& a, hipStream_t s);
 

@@ -169,7 +169,30 @@ def test_forward_quantized_argument_checks(bits, group, H, I, M, status):
                                    NULL, NULL, NULL, NULL, 0, ctypes.byref(info), NULL)
     assert st == status
     if status == 0:
-        assert info.variant == moe.MOE_VARIANT_PAIR_GEMV_QUANT and info.launches == 0
+        assert info.launches == 0
+        assert info.variant in (moe.MOE_VARIANT_PAIR_GEMV_QUANT, moe.MOE_VARIANT_STREAM_QUANT)
+
+
+@pytest.mark.parametrize("M,H,I,variant,launches", [
+    (1, 2048, 768, "pair", 4),          # M*top_k*4 <= E: per-pair GEMVs
+    (64, 2048, 768, "stream", 5),       # router, fused top-k + lists, GEMM 1, GEMM 2, sum
+    (512, 2048, 768, "stream", 7),      # 4096 pairs: top-k, count, scatter launches
+    (64, 2048 + 64, 768, "pair", 4),    # H % 128 != 0: per-pair GEMVs at any M
+    (64, 2048, 768 + 64, "pair", 4),
+])
+def test_forward_quantized_dispatch(M, H, I, variant, launches):
+    """The dispatch report is filled before any pointer is looked at."""
+    moe = _moe()
+    lib = moe.library()
+    qw = moe.QuantizedWeights(4, 64)
+    info = moe.DispatchInfo()
+    st = lib.moe_forward_quantized(NULL, NULL, NULL, ctypes.byref(qw), M, 128, 8, H, I, 1,
+                                   NULL, NULL, NULL, NULL, 0, ctypes.byref(info), NULL)
+    assert st == -1
+    want = moe.MOE_VARIANT_STREAM_QUANT if variant == "stream" else moe.MOE_VARIANT_PAIR_GEMV_QUANT
+    assert info.variant == want and info.launches == launches
+    assert info.block_m == (16 if variant == "stream" else 1)
+    assert info.sorted == int(variant == "stream")
 
 
 def test_forward_quantized_null_struct_and_workspace():

@@ -2,14 +2,22 @@
 64-element-group format of the MLX part of the page "SGLang issue #22283",
 4 and 8 bits) against the oracle's forward_quantized.
 
+Two kernel families: per-pair GEMVs up to E/2 pairs (M*top_k*2 <= E) and
+for shapes whose H or I is not a multiple of 128, and weight-streaming MFMA
+GEMMs over block_m 16 index lists above.
+
 Cases: the Qwen1.5-MoE shape whose down projection has K = 1408 (not a
 multiple of the kernels' 256- or 512-element passes, the case that thread
 asks about), the Qwen3-30B-A3B decode shape, and small layers whose H and I
 pick every per-lane unit count, several passes and ragged last passes, plus
-top_k above the eight waves of GEMV 2, renormalize off, and a larger batch
-(the path is correct for any M).  Same criteria as the bf16 layer: routing
-ids where the top-k margin exceeds 1e-4, weights to 1e-5, outputs within
-2e-2 max-abs (relative to max |ref|) and 5e-3 mean-relative.
+top_k above the eight waves of GEMV 2, renormalize off, and larger batches
+on both families: the streaming GEMMs at decode batches, with a K tail of
+half a slice, a one-slice GEMM 2, experts spanning many blocks (Zipf
+prior) and a two-segment index-list build.  Same criteria as the bf16
+layer: routing ids where the top-k margin exceeds 1e-4, the weights of the
+GPU's own ids to 1e-5, and every sampled token's output (near ties
+included, against the oracle's layer on the GPU's ids) within 2e-2 max-abs
+(relative to max |ref|) and 5e-3 mean-relative.
 """
 
 from __future__ import annotations
@@ -59,13 +67,31 @@ def run_quantized(ql: dict, ws=None, out=None):
     return out, ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64), info
 
 
-def check_quantized(ql: dict, n_tokens: int = 64, seed: int = 0, **kw):
+def streams(ql: dict) -> bool:
+    """Whether moe_forward_quantized takes the weight-streaming GEMMs."""
+    M, E, k, H, I = ql["M"], ql["E"], ql["top_k"], ql["H"], ql["I"]
+    return M * k * 2 > E and H % 128 == 0 and I % 128 == 0
+
+
+def check_dispatch(ql: dict, info: dict):
     moe = _moe()
+    if streams(ql):
+        P = ql["M"] * ql["top_k"]
+        route_launches = 2 if P <= 2048 else 4
+        assert info["variant"] == moe.MOE_VARIANT_STREAM_QUANT
+        assert info["sorted"] == 1 and info["block_m"] == 16
+        assert info["launches"] == route_launches + 3
+        assert info["k_tail"] == int(ql["H"] % 256 != 0)
+    else:
+        assert info["variant"] == moe.MOE_VARIANT_PAIR_GEMV_QUANT
+        assert info["launches"] == 4 and info["sorted"] == 0 and info["block_m"] == 1
+
+
+def check_quantized(ql: dict, n_tokens: int = 64, seed: int = 0, **kw):
     print(f"quantized case {ql['name']} M={ql['M']} E={ql['E']} k={ql['top_k']} "
           f"H={ql['H']} I={ql['I']} bits={ql['bits']}", flush=True)
     out, ids, wts, info = run_quantized(ql, **kw)
-    assert info["variant"] == moe.MOE_VARIANT_PAIR_GEMV_QUANT
-    assert info["launches"] == 4 and info["sorted"] == 0 and info["block_m"] == 1
+    check_dispatch(ql, info)
     toks = h.sample_tokens(ql["M"], n_tokens, seed)
     r = mo.route(ql["x"][toks], ql["w_router"], ql["top_k"], ql["renormalize"],
                  ql.get("logit_bias"))
@@ -116,8 +142,62 @@ def test_quantized_renormalize_off():
 
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quantized_larger_batch(bits):
-    """M = 64 of the Qwen3 decode shape: 512 pairs, each its own GEMV."""
-    check_quantized(wl.make_quantized_layer("qwen3_decode", 64, bits), n_tokens=24)
+    """M = 64 of the Qwen3 decode shape: 512 pairs on the streaming GEMMs."""
+    ql = wl.make_quantized_layer("qwen3_decode", 64, bits)
+    assert streams(ql)
+    check_quantized(ql, n_tokens=24)
+
+
+def test_quantized_pair_gemv_at_any_batch():
+    """H = 576 is not a multiple of 128: the per-pair GEMVs take every M."""
+    ql = wl.make_quantized_layer("toy", 48, 4, E=16, top_k=2, H=576, I=384, seed=77)
+    assert not streams(ql)
+    check_quantized(ql, n_tokens=24)
+
+
+# Streaming GEMMs: (name, M, bits, overrides)
+STREAM_CASES = [
+    ("qwen3_decode", 12, 4, {}),
+    ("qwen3_decode", 16, 8, {}),
+    ("qwen15", 16, 4, {}),                                      # I = 1408: 11 GEMM 2 slices
+    ("qwen15", 16, 8, {}),
+    ("toy", 8, 4, dict(E=8, top_k=2, H=1408, I=384)),          # K tail of half a slice
+    ("toy", 8, 8, dict(E=8, top_k=2, H=1408, I=384)),
+    ("toy", 40, 4, dict(E=16, top_k=4, H=256, I=128)),         # GEMM 2 in one slice
+    ("qwen3_prefill", 256, 4, {}),                              # Zipf: experts over many blocks
+    ("qwen3_prefill", 256, 8, {}),
+]
+
+
+@pytest.mark.parametrize("name,M,bits,over", STREAM_CASES,
+                         ids=lambda v: str(v) if not isinstance(v, dict) else
+                         "_".join(f"{k}{x}" for k, x in v.items()) or "model")
+def test_quantized_streaming(name, M, bits, over):
+    seed = {"seed": 3000 + M + bits} if over else {}
+    ql = wl.make_quantized_layer(name, M, bits, **over, **seed)
+    assert streams(ql)
+    check_quantized(ql, n_tokens=32)
+
+
+def test_quantized_streaming_two_segments():
+    """4096 pairs: the index lists are built by the two-kernel align."""
+    ql = wl.make_quantized_layer("toy", 512, 4, E=64, top_k=8, H=256, I=256, seed=3100)
+    assert streams(ql) and ql["M"] * ql["top_k"] > 2048
+    check_quantized(ql, n_tokens=32)
+
+
+def test_quantized_streaming_poisoned_workspace_repeatable():
+    """Workspace filled with 0xFF bytes, then reused: identical outputs."""
+    import torch
+    ql = wl.make_quantized_layer("qwen3_decode", 16, 4)
+    moe = _moe()
+    nbytes = moe.moe_workspace_size(ql["M"], ql["E"], ql["top_k"], ql["H"], ql["I"])
+    ws = torch.full((nbytes,), -1, dtype=torch.uint8, device="cuda")
+    a, _, _, info = run_quantized(ql, ws=ws)
+    assert info["variant"] == moe.MOE_VARIANT_STREAM_QUANT
+    b, _, _, _ = run_quantized(ql, ws=ws)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check_quantized(ql, n_tokens=16, ws=ws)
 
 
 def test_quantized_poisoned_workspace_and_output():
