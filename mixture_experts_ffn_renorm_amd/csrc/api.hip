@@ -557,9 +557,9 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
     fill_info(info, B, H, I, M == 0 ? 0 : kPairGemvForwardLaunches, 0);
     if (info != nullptr) info->variant = MOE_VARIANT_PAIR_GEMV_MXFP8;
   } else {
-    // GEMM 1, quantize act, then GEMM 2 and its per-token sum (x is
-    // quantized by the top-k launch)
-    fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 2 + kGemm2Launches);
+    // GEMM 1, quantize act (in GEMM 1's epilogue at block_m 16), then GEMM 2
+    // and its per-token sum (x is quantized by the top-k launch)
+    fill_info(info, B, H, I, M == 0 ? 0 : route_launches + (B == 16 ? 1 : 2) + kGemm2Launches);
     if (info != nullptr)
       info->variant = B == 16 ? MOE_VARIANT_STREAM_MXFP8 : MOE_VARIANT_TILED_MXFP8;
   }
@@ -624,8 +624,13 @@ int moe_forward_mxfp8(const uint16_t* x, const uint16_t* w_router, const float* 
   g.w = reinterpret_cast<const uint16_t*>(w->w13_codes);
   g.w_scales = w->w13_scales;
   g.out = act;
-  MOE_TRY_HIP(B == 16 ? launch_gemm1_stream(g, s) : launch_gemm1_tiled(g, s));
-  MOE_TRY_HIP(launch_mx_quantize(act, M * top_k, I, qact, sact, s));
+  if (B == 16) {
+    // the streaming GEMM 1 quantizes act in its epilogue
+    MOE_TRY_HIP(launch_gemm1_stream_mx_quantize(g, qact, sact, s));
+  } else {
+    MOE_TRY_HIP(launch_gemm1_tiled(g, s));
+    MOE_TRY_HIP(launch_mx_quantize(act, M * top_k, I, qact, sact, s));
+  }
   g.a_src = reinterpret_cast<const uint16_t*>(qact);
   g.a_scales = sact;
   g.w = reinterpret_cast<const uint16_t*>(w->w2_codes);

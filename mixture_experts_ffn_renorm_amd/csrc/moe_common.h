@@ -430,6 +430,11 @@ hipError_t launch_mx_quantize(const uint16_t* src, int rows, int K, uint8_t* cod
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm1_stream(const GemmArgs& a, hipStream_t s);
+// MXFP8 streaming GEMM 1 (block_m 16; a_src / a_scales: x codes and scales)
+// that writes act already quantized: codes qact [P, I] and E8M0 scales
+// sact [P, I/32] (I % 32 == 0, H % 128 == 0).
+hipError_t launch_gemm1_stream_mx_quantize(const GemmArgs& a, uint8_t* qact, uint8_t* sact,
+                                           hipStream_t s);
 hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s);
 // out[t] = bf16(sum over slots j of partial[t*top_k + j]), j ascending.
 hipError_t launch_combine_partials(const float* partial, int M, int top_k, int H, uint16_t* out,
