@@ -237,13 +237,14 @@ def test_route_deterministic():
 # the index lists moe_forward builds from its own routing
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [16, 64, 256, 512])
+@pytest.mark.parametrize("M", [5, 16, 17, 64, 256, 512])
 def test_forward_index_lists_bit_exact(M):
     """The lists moe_forward leaves in its workspace equal oracle.align of
     the GPU's own topk_ids, bit for bit: the fused top-k + index-list launch
-    with one workgroup (16 tokens), several (64), the most a one-segment
-    batch takes (256 tokens = 2048 pairs), and the two-kernel align of a
-    multi-segment batch (512)."""
+    with two workgroups of four tokens (5 tokens, the second short), several
+    (16, 17: five workgroups with the last one short, 64), the most a
+    one-segment batch takes (256 tokens = 2048 pairs), and the two-kernel
+    align of a multi-segment batch (512)."""
     import torch
     moe = _moe()
     lay = wl.make_layer("qwen3_decode", M)
