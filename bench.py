@@ -52,7 +52,7 @@ PREFILL_WORKLOAD = ("qwen3_prefill", 4096)
 
 
 VARIANT_NAMES = {0: "tiled", 1: "stream", 2: "pair_gemv", 3: "pair_gemv_quant", 4: "tiled_mxfp8",
-                 5: "stream_mxfp8", 6: "pair_gemv_mxfp8", 7: "stream_quant"}
+                 5: "stream_mxfp8", 6: "pair_gemv_mxfp8", 7: "stream_quant", 8: "tiled_quant"}
 
 
 def parse_args():

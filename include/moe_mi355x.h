@@ -76,6 +76,8 @@ typedef enum moe_status {
                                           weights and inputs (M*top_k*4 <= E, no lists) */
 #define MOE_VARIANT_STREAM_QUANT 7  /* moe_forward_quantized: weight-streaming MFMA
                                        GEMMs on group-quantized weights (block_m 16) */
+#define MOE_VARIANT_TILED_QUANT 8  /* moe_forward_quantized: LDS-tiled MFMA GEMMs, the
+                                      codes widened to bf16 tiles in LDS (block_m 128) */
 typedef struct moe_dispatch_info {
   int variant;   /* MOE_VARIANT_* of the GEMMs                                   */
   int block_m;   /* rows (pairs) per block of the index lists                    */
@@ -318,7 +320,12 @@ typedef struct moe_quantized_weights {
  * fp32 per group; GEMM 2 writes fp32 weighted pair-order rows and a second
  * kernel sums them per token (info->variant MOE_VARIANT_STREAM_QUANT,
  * info->sorted 1).  The streaming kernels need H and I to be multiples of
- * 128; other shapes run the per-pair GEMVs at every M.
+ * 128 (other shapes run the per-pair GEMVs there).  Where moe_forward runs
+ * its tiles, the quantized layer runs the same copy-wave tiles over block_m
+ * 128 lists with each stage's codes widened by the copy waves into bf16
+ * weight tiles in LDS (w = s*q + b rounded once to bf16, as a quantized
+ * matmul in the activation dtype does) and GEMM 2's bf16 pair-order rows
+ * summed per token (info->variant MOE_VARIANT_TILED_QUANT).
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, workspace:
  *                as for moe_forward (same workspace size)

@@ -30,6 +30,7 @@ MOE_VARIANT_TILED_MXFP8 = 4
 MOE_VARIANT_STREAM_MXFP8 = 5
 MOE_VARIANT_PAIR_GEMV_MXFP8 = 6
 MOE_VARIANT_STREAM_QUANT = 7
+MOE_VARIANT_TILED_QUANT = 8
 
 _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int

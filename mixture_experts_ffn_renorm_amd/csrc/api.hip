@@ -417,13 +417,19 @@ int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const flo
   if (qw == nullptr) return MOE_ERR_INVALID_ARG;
   if ((qw->bits != 4 && qw->bits != 8) || qw->group_size != 64) return MOE_ERR_UNSUPPORTED;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  // per-pair GEMVs up to E/2 pairs (and for shapes the streaming kernels do
-  // not take), weight-streaming GEMMs over block_m 16 index lists above.
+  // per-pair GEMVs up to E/2 pairs, weight-streaming GEMMs over block_m 16
+  // index lists (per-pair GEMVs instead for shapes the streaming kernels do
+  // not take), the copy-wave tiles with the codes widened in LDS over
+  // block_m 128 lists where the bf16 layer runs 128- or 256-pair tiles.
   // Measured on the Qwen3 shape (E = 128, top_k = 8): 8 tokens 63 / 71 us
   // per-pair against 69 / 81 streaming (4 / 8 bits), 16 tokens 103 / 129
   // against 84 / 102.
-  const bool per_pair = (long long)M * top_k * 2 <= E || !qgemm_stream_shapes_ok(H, I);
-  const int B = per_pair ? 1 : 16;
+  int B = 1;
+  if ((long long)M * top_k * 2 > E) {
+    if (moe_pick_block_m(M, E, top_k) >= 128) B = 128;
+    else if (qgemm_stream_shapes_ok(H, I)) B = 16;
+  }
+  const bool per_pair = B == 1;
   const int route_launches = fused_route(M, top_k) ? 2 : 2 + (align_segments(M * top_k) > 1 ? 2 : 1);
   if (per_pair) {
     fill_info(info, 1, H, I, M == 0 ? 0 : kPairGemvForwardLaunches, 0);
@@ -431,9 +437,9 @@ int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const flo
   } else {
     fill_info(info, B, H, I, M == 0 ? 0 : route_launches + 1 + kGemm2Launches);
     if (info != nullptr) {
-      info->variant = MOE_VARIANT_STREAM_QUANT;
-      info->block_k = 256;
-      info->k_tail = H % 256 != 0 ? 1 : 0;
+      info->variant = B == 16 ? MOE_VARIANT_STREAM_QUANT : MOE_VARIANT_TILED_QUANT;
+      info->block_k = B == 16 ? 256 : kTiledBK;
+      info->k_tail = H % info->block_k != 0 ? 1 : 0;
     }
   }
   if (M == 0) return MOE_OK;
@@ -479,8 +485,13 @@ int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const flo
               qw->w2_biases, sorted, eids, boff, wts, M, top_k, E, H, I, qw->bits,
               (int)max_blocks((long long)M * top_k, E, B), act,
               reinterpret_cast<float*>(ws + L.partial), out};
-  MOE_TRY_HIP(launch_qgemm1_stream(g, s));
-  MOE_TRY_HIP(launch_qgemm2_stream(g, s));
+  if (B == 16) {
+    MOE_TRY_HIP(launch_qgemm1_stream(g, s));
+    MOE_TRY_HIP(launch_qgemm2_stream(g, s));
+  } else {
+    MOE_TRY_HIP(launch_qgemm1_tiled(g, s));
+    MOE_TRY_HIP(launch_qgemm2_tiled(g, s));
+  }
   return MOE_OK;
 }
 

@@ -141,16 +141,34 @@ struct TileParams {
   int M, top_k, E, H, I;
   int ntn;                 // column tiles per block
   uint16_t* out;           // GEMM 1: act [P, I]; GEMM 2: pair-order product [P, H]
+  // group-quantized weights (QB = 4 or 8): codes [rows, K*QB/8], bf16 scales
+  // and biases [rows, K/64]
+  const uint8_t* wq;
+  const uint8_t* wsc;
+  const uint8_t* wbi;
 };
 
-template <int BM, bool kGemm1, bool kMX, bool kPC = false>
+// QB = 4 or 8: the weights are group-quantized codes (copy-wave tiles,
+// BM = 128 only); see the quantized ring below.
+template <int BM, bool kGemm1, bool kMX, bool kPC = false, int QB = 0>
 __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_tiled_kernel(
     const TileParams prm) {
   using C = TileCfg<BM, kMX, kPC>;
+  static_assert(QB == 0 || (kPC && !kMX && BM == 128), "quantized tiles: copy waves, 128 pairs");
   constexpr int NT = C::kNT;
   constexpr int kStages = C::kStages;
   constexpr int kBN = C::kBN;
   constexpr int kHalf = kBN / 2;   // GEMM 1: gate rows, then as many up rows
+  // Quantized ring (QB > 0): A slots hold the stage's widened bf16 weight
+  // rows, B slots the gathered pair rows, code slots the stage's packed codes
+  // (kBN rows x 64 * QB / 8 bytes) and scale slots one 32-bit word of the
+  // scales, then of the biases, per weight row (the aligned word holding the
+  // stage's group value).
+  constexpr int kQASlot = kBN * kRowBytes;                      // 32 KB
+  constexpr int kQBSlot = BM * kRowBytes;                       // 16 KB
+  constexpr int kQCB = kBK * (QB > 0 ? QB : 8) / 8;             // code bytes per row and stage
+  constexpr int kQCSlot = kBN * kQCB;                           // 8 / 16 KB
+  constexpr int kQSSlot = kBN * 4 * 2;                          // 2 KB
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ __attribute__((aligned(16))) int s_pair[kMeta][BM];
   __shared__ int s_exp[kMeta];
@@ -307,7 +325,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   for (int s = 0; s < 2; ++s) {
     const int slot = ((s * 4 + kg) ^ swz(r16)) << 4;
     abase[s] = (arow0 + r16) * kRowBytes + slot;
-    bbase[s] = (kBN + wp * QS + r16) * kRowBytes + slot;
+    bbase[s] = (wp * QS + r16) * kRowBytes + slot;   // from the B operand's first row
   }
   auto aconst = [](int i) {
     return (kGemm1 ? (i >> 1) * kHalf + (i & 1) * 16 : 16 * i) * kRowBytes;
@@ -330,6 +348,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   // is chunks kg and 4 + kg of its row, its scale byte that of k block kg.
   auto compute_mx = [&](const uint8_t* sb) {
     const uint8_t* sc = sb + C::kOperandBytes;
+    const uint8_t* sbB = sb + kBN * kRowBytes;
     i32x8 af[4];
     int sa[4];
 #pragma unroll
@@ -346,8 +365,8 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
 #pragma unroll
       for (int j = 0; j < TQ; ++j) {
         const int off = (q * 2 * QS + 16 * j) * kRowBytes;
-        const i32x8 bfr = cat_u32x4(*reinterpret_cast<const u32x4*>(sb + bbase[0] + off),
-                                    *reinterpret_cast<const u32x4*>(sb + bbase[1] + off));
+        const i32x8 bfr = cat_u32x4(*reinterpret_cast<const u32x4*>(sbB + bbase[0] + off),
+                                    *reinterpret_cast<const u32x4*>(sbB + bbase[1] + off));
         const int sbv = sc[(kBN + wp * QS + q * 2 * QS + 16 * j + r16) * 4 + kg];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -355,8 +374,9 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       }
     }
   };
-  // One stage of MFMAs over this wave's active quarters, fully unrolled.
-  auto compute = [&](const uint8_t* sb) {
+  // One stage of MFMAs over this wave's active quarters, fully unrolled;
+  // sb holds the A rows (weights) and sbB the B rows (pairs) of the stage.
+  auto compute = [&](const uint8_t* sb, const uint8_t* sbB) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 af[4];
@@ -373,7 +393,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
           u32x4 bfr[JB];
 #pragma unroll
           for (int j = 0; j < JB; ++j)
-            bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] +
+            bfr[j] = *reinterpret_cast<const u32x4*>(sbB + bbase[s] +
                                                      (q * 2 * QS + 16 * (j0 + j)) * kRowBytes);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -386,7 +406,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   };
   // Consumption of stage g by an MFMA wave (after the stage's barrier):
   // MFMAs, and the tile epilogue after the tile's last k step.
-  int c_i = 0, c_kt = 0, c_buf = 0, c_slot = 0;
+  int c_i = 0, c_kt = 0, c_buf = 0, c_slot = 0, c_g = 0;
   auto consume = [&]() {
     const int i_tile = c_i, kt = c_kt;
     const int buf = c_buf;
@@ -396,10 +416,18 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       act0 = __ballot(v0) != 0ull;
       act1 = __ballot(v1) != 0ull;
     }
-    const uint8_t* sb = ring + c_slot * C::kStageBytes;
-    if (act0 || act1) {
-      if constexpr (kMX) compute_mx(sb); else compute(sb);
+    if constexpr (QB > 0) {
+      // quantized ring: A (widened weights) in two slots, B in three
+      const uint8_t* sa = ring + (c_g & 1) * kQASlot;
+      const uint8_t* sbb = ring + 2 * kQASlot + (c_g % 3) * kQBSlot;
+      if (act0 || act1) compute(sa, sbb);
+    } else {
+      const uint8_t* sb = ring + c_slot * C::kStageBytes;
+      if (act0 || act1) {
+        if constexpr (kMX) compute_mx(sb); else compute(sb, sb + kBN * kRowBytes);
+      }
     }
+    ++c_g;
     c_slot = c_slot == kStages - 1 ? 0 : c_slot + 1;
     if (++c_kt == nk) { c_kt = 0; ++c_i; c_buf = c_buf == kMeta - 1 ? 0 : c_buf + 1; }
     if (kt != nk - 1) return;
@@ -490,10 +518,144 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
     }
   };
 
+  // ---- quantized weights (QB > 0): the copy waves' loop ----
+  // Per stage g (64 k of tile g / nk): DMA of the stage's codes, the scale
+  // and bias words of its 256 weight rows and the gathered pair rows; once
+  // they have landed, each copy lane widens one weight row, w = s q + b
+  // rounded to bf16, into the stage's A slot in the layout the copies of
+  // bf16 weights give (chunk c of row R at slot c ^ swz(R)).  The A rows of
+  // stage g + 1 are widened while the MFMA waves multiply stage g.
+  auto quant_copier = [&]() {
+    if constexpr (QB > 0) {
+      constexpr int kQI = kQCSlot / 1024 / C::kCopyWaves;   // code copies per wave and stage
+      constexpr int kQRows = 1024 / kQCB;                  // code rows per copy
+      constexpr int kQChunks = kQCB / 16;                  // 16-byte chunks per code row and stage
+      constexpr int kQC = kQI + C::kXGroups + 2;           // copies per wave and stage
+      uint8_t* const qa = ring;                            // 2 A slots
+      uint8_t* const qb = ring + 2 * kQASlot;              // 3 B slots
+      uint8_t* const qc = qb + 3 * kQBSlot;                // 2 code slots
+      uint8_t* const qs = qc + 2 * kQCSlot;                // 2 scale slots
+      const int rowq = Ke * QB / 8;                        // code bytes per weight row
+      const int ng = Ke / 64;
+      const int R = cw * 64 + lane;                        // the weight row this lane widens
+      // global weight row of tile row r (or -1 past the weights)
+      auto wrow = [&](int nt, int e, int r) -> long long {
+        if (kGemm1) {
+          const int f = nt * kHalf + (r % kHalf);
+          return f < prm.I ? (long long)e * 2 * prm.I + (r < kHalf ? f : prm.I + f) : -1;
+        }
+        const int h = nt * kBN + r;
+        return h < prm.H ? (long long)e * prm.H + h : -1;
+      };
+      const uint8_t* csrc[kQI];
+      const uint8_t* ssrc = nullptr;
+      const uint8_t* bsrc = nullptr;
+      long long srow = -1;                                 // this lane's scale row (R)
+      int par0 = 0, par1 = 0;                              // half of the scale word, per code slot
+      int q_i = 0, q_kt = 0;
+      auto qissue = [&](int g) {
+        if (q_kt == 0) {
+          setup(q_i);                                      // pair-row sources, metadata
+          const int buf = q_i % kMeta;
+          const int j = j0 + q_i * nslots;
+          const int nt = j - (j / ntn) * ntn;
+          const int e = s_exp[buf];
+#pragma unroll
+          for (int q = 0; q < kQI; ++q) {
+            const int r = (cw * kQI + q) * kQRows + lane / kQChunks;
+            const long long wr = wrow(nt, e, r);
+            csrc[q] = wr >= 0 ? prm.wq + wr * rowq + (lane % kQChunks) * 16 : nullptr;
+          }
+          srow = wrow(nt, e, R);
+          ssrc = srow >= 0 ? prm.wsc : nullptr;
+          bsrc = srow >= 0 ? prm.wbi : nullptr;
+        }
+        const int kt = q_kt;
+        if (++q_kt == nk) { q_kt = 0; ++q_i; }
+        uint8_t* cdst = qc + (g & 1) * kQCSlot;
+#pragma unroll
+        for (int q = 0; q < kQI; ++q)
+          load_lds16<kNonTemporal>(csrc[q] != nullptr ? (const void*)(csrc[q] + kt * kQCB)
+                                                      : (const void*)kZeroPage,
+                                   cdst + (cw * kQI + q) * 1024);
+        uint8_t* bdst = qb + (g % 3) * kQBSlot;
+#pragma unroll
+        for (int gi = 0; gi < C::kXGroups; ++gi) {
+          load_lds16(xsrc[gi], bdst + (cw + C::kCopyWaves * gi) * 8 * kRowBytes);
+          xsrc[gi] += xstep[gi];
+        }
+        // the aligned 32-bit word that holds group kt of row R, and its half
+        const long long word = srow >= 0 ? ((srow * ng + kt) & ~1ll) : 0;
+        const int par = srow >= 0 ? (int)((srow * ng + kt) & 1) : 0;
+        if (g & 1) par1 = par; else par0 = par;
+        uint8_t* sdst = qs + (g & 1) * kQSSlot;
+        load_lds4(ssrc != nullptr ? (const void*)(ssrc + word * 2) : (const void*)kZeroPage,
+                  sdst + cw * 256);
+        load_lds4(bsrc != nullptr ? (const void*)(bsrc + word * 2) : (const void*)kZeroPage,
+                  sdst + 1024 + cw * 256);
+      };
+      auto widen = [&](int g) {
+        const uint8_t* cr = qc + (g & 1) * kQCSlot + R * kQCB;
+        const uint8_t* ss = qs + (g & 1) * kQSSlot;
+        const uint32_t swd = *reinterpret_cast<const uint32_t*>(ss + R * 4);
+        const uint32_t bwd = *reinterpret_cast<const uint32_t*>(ss + 1024 + R * 4);
+        const int par = (g & 1) ? par1 : par0;
+        const float sc = par ? bf16_hi(swd) : bf16_lo(swd);
+        const float bi = par ? bf16_hi(bwd) : bf16_lo(bwd);
+        uint8_t* arow = qa + (g & 1) * kQASlot + R * kRowBytes;
+        u32x4 cw4[kQCB / 16];
+#pragma unroll
+        for (int i = 0; i < kQCB / 16; ++i) cw4[i] = *reinterpret_cast<const u32x4*>(cr + 16 * i);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {      // 8 values a chunk, 8 chunks of 64 k
+          float v[8];
+          if constexpr (QB == 4) {
+            // nibble 2j is byte j of lo, nibble 2j + 1 byte j of hi
+            const uint32_t w = cw4[c >> 2][c & 3];
+            const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              v[2 * k] = (float)((lo >> (8 * k)) & 255u);
+              v[2 * k + 1] = (float)((hi >> (8 * k)) & 255u);
+            }
+          } else {
+            const uint32_t w0 = cw4[c >> 1][(c & 1) * 2], w1 = cw4[c >> 1][(c & 1) * 2 + 1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              v[k] = (float)((w0 >> (8 * k)) & 255u);
+              v[4 + k] = (float)((w1 >> (8 * k)) & 255u);
+            }
+          }
+          u32x4 o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            o[k] = pack_bf16x2(__builtin_fmaf(sc, v[2 * k], bi), __builtin_fmaf(sc, v[2 * k + 1], bi));
+          *reinterpret_cast<u32x4*>(arow + ((c ^ swz(R)) << 4)) = o;
+        }
+      };
+      qissue(0);
+      if (G > 1) qissue(1);
+      if (G > 1) wait_vmem<kQC>(); else wait_vmem<0>();
+      widen(0);
+      for (int g = 0; g < G; ++g) {
+        wait_lgkm0();        // this lane's A rows of stage g are in LDS
+        barrier_nofence();   // stage g is complete; stage g-1 has been consumed
+        if (g + 2 < G) qissue(g + 2);
+        if (g + 1 < G) {
+          // stage g + 1's copies have landed once at most stage g + 2's are pending
+          if (g + 2 < G) wait_vmem<kQC>(); else wait_vmem<0>();
+          widen(g + 1);
+        }
+      }
+    }
+  };
+
   if constexpr (kPC) {
     // Copy waves and MFMA waves run separate loops with the same barriers,
     // so neither keeps the other's registers live.
-    if (copier) {
+    if (copier && QB > 0) {
+      quant_copier();
+    } else if (copier) {
 #pragma unroll
       for (int g = 0; g < kStages - 1; ++g)
         if (g < G) issue_stage();
@@ -555,11 +717,12 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __res
   *reinterpret_cast<u32x4*>(out + (size_t)t * H + h) = o;
 }
 
-template <int BM, bool kGemm1, bool kMX = false, bool kPC = false>
-hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* out) {
+template <int BM, bool kGemm1, bool kMX = false, bool kPC = false, int QB = 0>
+hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* out,
+                        const moe_host::QGemmArgs* q = nullptr) {
   using C = TileCfg<BM, kMX, kPC>;
   constexpr int kBN = C::kBN;
-  TileParams prm;
+  TileParams prm{};
   prm.a_src = a.a_src;
   prm.w = a.w;
   prm.a_scales = a.a_scales;
@@ -574,17 +737,26 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* ou
   prm.I = a.I;
   prm.ntn = kGemm1 ? moe_host::ceil_div_host(a.I, kBN / 2) : moe_host::ceil_div_host(a.H, kBN);
   prm.out = out;
+  if (QB > 0) {
+    prm.wq = reinterpret_cast<const uint8_t*>(kGemm1 ? q->w13q : q->w2q);
+    prm.wsc = reinterpret_cast<const uint8_t*>(kGemm1 ? q->w13_scales : q->w2_scales);
+    prm.wbi = reinterpret_cast<const uint8_t*>(kGemm1 ? q->w13_biases : q->w2_biases);
+    prm.w = reinterpret_cast<const uint16_t*>(prm.wq);   // (no bf16 weights are read)
+  }
   // persistent grid: one workgroup per CU, never more than the tiles, a multiple of 8
   const long long tiles = (long long)a.max_blocks * prm.ntn;
   long long grid = std::min<long long>(tiles, moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
-  const size_t lds = C::kRingBytes;
+  // quantized ring: 2 A slots, 3 B slots, 2 code slots, 2 scale slots
+  const size_t lds = QB > 0 ? (size_t)2 * kBN * kRowBytes + 3 * BM * kRowBytes +
+                                  2 * kBN * (kBK * QB / 8) + 2 * kBN * 8
+                            : C::kRingBytes;
   static bool lds_set[moe_host::kMaxDevices] = {};
   const hipError_t err = moe_host::ensure_dynamic_lds(
-      reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX, kPC>), (int)lds, lds_set);
+      reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX, kPC, QB>), (int)lds, lds_set);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX, kPC>), dim3((unsigned)grid), dim3(C::kThreadsT),
-                     lds, s, prm);
+  hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX, kPC, QB>), dim3((unsigned)grid),
+                     dim3(C::kThreadsT), lds, s, prm);
   return hipGetLastError();
 }
 
@@ -601,6 +773,44 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t s) {
   if (a.block_m == 256) return launch_tiled<256, true, false, true>(a, s, a.out);
   if (a.block_m == 128) return launch_tiled<128, true, false, true>(a, s, a.out);
   return launch_tiled<64, true, false, true>(a, s, a.out);
+}
+
+namespace {
+GemmArgs quant_gemm_args(const QGemmArgs& q) {
+  GemmArgs a{};
+  a.sorted_token_ids = q.sorted_token_ids;
+  a.expert_ids = q.expert_ids;
+  a.expert_block_offsets = q.expert_block_offsets;
+  a.topk_weights = q.topk_weights;
+  a.M = q.M;
+  a.top_k = q.top_k;
+  a.E = q.E;
+  a.H = q.H;
+  a.I = q.I;
+  a.block_m = 128;
+  a.max_blocks = q.max_blocks;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_qgemm1_tiled(const QGemmArgs& q, hipStream_t s) {
+  GemmArgs a = quant_gemm_args(q);
+  a.a_src = q.x;
+  return q.bits == 4 ? launch_tiled<128, true, false, true, 4>(a, s, q.act, &q)
+                     : launch_tiled<128, true, false, true, 8>(a, s, q.act, &q);
+}
+
+hipError_t launch_qgemm2_tiled(const QGemmArgs& q, hipStream_t s) {
+  GemmArgs a = quant_gemm_args(q);
+  a.a_src = q.act;
+  uint16_t* rows = reinterpret_cast<uint16_t*>(q.partial);
+  const hipError_t err = q.bits == 4 ? launch_tiled<128, false, false, true, 4>(a, s, rows, &q)
+                                     : launch_tiled<128, false, false, true, 8>(a, s, rows, &q);
+  if (err != hipSuccess) return err;
+  const long long n8 = (long long)q.M * (q.H / 8);
+  hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, rows,
+                     q.topk_weights, q.M, q.top_k, q.H, q.out);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {

@@ -45,7 +45,6 @@ constexpr int kG2Cols = 4;     // GEMV 2: output columns per workgroup (divides 
 // dot-2 instruction takes two adjacent elements of each operand as they sit
 // in memory (products exact in fp32, accumulated in fp32), so nothing is
 // unpacked.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // (the words come in by value: a bit cast of a vector-element lvalue would
 // read the vector's first element)

@@ -31,16 +31,18 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (lo in the low half), round to nearest
+// even, NaN stays NaN: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // SiLU(g) * u with SiLU(g) = g / (1 + exp(-g)).
@@ -85,6 +87,12 @@ __device__ __forceinline__ void wait_vmem() {
   // lgkmcnt (11:8) left at their maxima, i.e. not waited on.
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until this wave's LDS operations have completed (vmcnt and expcnt
+// left at their maxima, i.e. not waited on).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
 // Workgroup barrier without a memory fence (a fenced barrier also waits for
@@ -522,6 +530,11 @@ struct QGemmArgs {
 bool qgemm_stream_shapes_ok(int H, int I);
 hipError_t launch_qgemm1_stream(const QGemmArgs& a, hipStream_t s);
 hipError_t launch_qgemm2_stream(const QGemmArgs& a, hipStream_t s);
+// The same GEMMs on the copy-wave tiles (block_m 128; H and I multiples of
+// 64): the copy waves widen each stage's codes into bf16 weight tiles in
+// LDS.  GEMM 2 writes bf16 pair-order rows into partial and sums them into out.
+hipError_t launch_qgemm1_tiled(const QGemmArgs& a, hipStream_t s);
+hipError_t launch_qgemm2_tiled(const QGemmArgs& a, hipStream_t s);
 
 hipError_t launch_pair_gemv1(const PairGemvArgs& a, hipStream_t s);
 hipError_t launch_pair_gemv2(const PairGemvArgs& a, hipStream_t s);

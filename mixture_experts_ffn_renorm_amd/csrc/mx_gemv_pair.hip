@@ -39,7 +39,6 @@ constexpr int kG1Waves = 4;
 constexpr int kMaxWaves = 8;   // GEMV 2 waves: min(top_k, 8)
 constexpr int kG2Rows = 4;     // GEMV 2 output columns per workgroup
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // fp32 values of the E4M3 bytes 0, 1 (kHi = false) or 2, 3 (kHi = true) of w
 template <bool kHi>

@@ -68,7 +68,6 @@ __device__ __forceinline__ float sum_unit(const u32x4* xv) {
 // pair, and sum (128 + q_i) x_i - 128 * sum x_i = sum q_i x_i.  Code word w
 // holds elements 8w .. 8w + 7; its pair i (i < 4) takes elements i and
 // i + 4 (bits 4i and 16 + 4i), and x is regrouped once per unit to match.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),

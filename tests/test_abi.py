@@ -179,6 +179,9 @@ def test_forward_quantized_argument_checks(bits, group, H, I, M, status):
     (512, 2048, 768, "stream", 7),      # 4096 pairs: top-k, count, scatter launches
     (64, 2048 + 64, 768, "pair", 4),    # H % 128 != 0: per-pair GEMVs at any M
     (64, 2048, 768 + 64, "pair", 4),
+    (1024, 2048, 768, "tiled", 7),      # 64 pairs per expert: bf16 tiles widened in LDS
+    (4096, 2048, 768, "tiled", 7),
+    (1024, 2048 + 64, 768 + 64, "tiled", 7),   # the tiles take H, I % 64
 ])
 def test_forward_quantized_dispatch(M, H, I, variant, launches):
     """The dispatch report is filled before any pointer is looked at."""
@@ -189,10 +192,11 @@ def test_forward_quantized_dispatch(M, H, I, variant, launches):
     st = lib.moe_forward_quantized(NULL, NULL, NULL, ctypes.byref(qw), M, 128, 8, H, I, 1,
                                    NULL, NULL, NULL, NULL, 0, ctypes.byref(info), NULL)
     assert st == -1
-    want = moe.MOE_VARIANT_STREAM_QUANT if variant == "stream" else moe.MOE_VARIANT_PAIR_GEMV_QUANT
+    want = {"stream": moe.MOE_VARIANT_STREAM_QUANT, "tiled": moe.MOE_VARIANT_TILED_QUANT,
+            "pair": moe.MOE_VARIANT_PAIR_GEMV_QUANT}[variant]
     assert info.variant == want and info.launches == launches
-    assert info.block_m == (16 if variant == "stream" else 1)
-    assert info.sorted == int(variant == "stream")
+    assert info.block_m == {"stream": 16, "tiled": 128, "pair": 1}[variant]
+    assert info.sorted == int(variant != "pair")
 
 
 def test_forward_quantized_null_struct_and_workspace():

@@ -67,17 +67,28 @@ def run_quantized(ql: dict, ws=None, out=None):
     return out, ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64), info
 
 
+def tiles(ql: dict) -> bool:
+    """Whether moe_forward_quantized takes the LDS-tiled GEMMs (block_m 128)."""
+    M, E, k = ql["M"], ql["E"], ql["top_k"]
+    return M * k * 2 > E and _moe().moe_pick_block_m(M, E, k) >= 128
+
+
 def streams(ql: dict) -> bool:
     """Whether moe_forward_quantized takes the weight-streaming GEMMs."""
     M, E, k, H, I = ql["M"], ql["E"], ql["top_k"], ql["H"], ql["I"]
-    return M * k * 2 > E and H % 128 == 0 and I % 128 == 0
+    return M * k * 2 > E and not tiles(ql) and H % 128 == 0 and I % 128 == 0
 
 
 def check_dispatch(ql: dict, info: dict):
     moe = _moe()
-    if streams(ql):
-        P = ql["M"] * ql["top_k"]
-        route_launches = 2 if P <= 2048 else 4
+    P = ql["M"] * ql["top_k"]
+    route_launches = 2 if P <= 2048 else 4
+    if tiles(ql):
+        assert info["variant"] == moe.MOE_VARIANT_TILED_QUANT
+        assert info["sorted"] == 1 and info["block_m"] == 128
+        assert info["launches"] == route_launches + 3
+        assert info["k_tail"] == 0
+    elif streams(ql):
         assert info["variant"] == moe.MOE_VARIANT_STREAM_QUANT
         assert info["sorted"] == 1 and info["block_m"] == 16
         assert info["launches"] == route_launches + 3
@@ -181,9 +192,49 @@ def test_quantized_streaming(name, M, bits, over):
 
 def test_quantized_streaming_two_segments():
     """4096 pairs: the index lists are built by the two-kernel align."""
-    ql = wl.make_quantized_layer("toy", 512, 4, E=64, top_k=8, H=256, I=256, seed=3100)
+    ql = wl.make_quantized_layer("toy", 512, 4, E=128, top_k=8, H=256, I=256, seed=3100)
     assert streams(ql) and ql["M"] * ql["top_k"] > 2048
     check_quantized(ql, n_tokens=32)
+
+
+# LDS-tiled GEMMs on codes widened in LDS: (name, M, bits, overrides)
+TILED_CASES = [
+    ("qwen3_prefill", 1024, 4, {}),                             # Zipf: 1 .. many blocks per expert
+    ("qwen3_prefill", 1024, 8, {}),
+    ("qwen15", 1024, 4, {}),                                    # I = 1408: 22 k stages in GEMM 2
+    ("toy", 200, 4, dict(E=8, top_k=2, H=576, I=320)),         # H, I % 64 only; N tails
+    ("toy", 200, 8, dict(E=8, top_k=2, H=576, I=320)),
+    ("toy", 300, 4, dict(E=4, top_k=1, H=64, I=64)),           # one k stage: one stage per tile
+    ("toy", 300, 8, dict(E=4, top_k=1, H=64, I=64)),
+]
+
+
+@pytest.mark.parametrize("name,M,bits,over", TILED_CASES,
+                         ids=lambda v: str(v) if not isinstance(v, dict) else
+                         "_".join(f"{k}{x}" for k, x in v.items()) or "model")
+def test_quantized_tiled(name, M, bits, over):
+    seed = {"seed": 3200 + M + bits} if over else {}
+    ql = wl.make_quantized_layer(name, M, bits, **over, **seed)
+    assert tiles(ql)
+    check_quantized(ql, n_tokens=32)
+
+
+def test_quantized_tiled_poisoned_workspace_repeatable():
+    """Workspace and output filled with 0xFF bytes, then reused: identical
+    outputs on the tiled path."""
+    import torch
+    moe = _moe()
+    ql = wl.make_quantized_layer("toy", 256, 4, E=16, top_k=4, H=512, I=256, seed=3300)
+    assert tiles(ql)
+    nbytes = moe.moe_workspace_size(ql["M"], ql["E"], ql["top_k"], ql["H"], ql["I"])
+    ws = torch.full((nbytes,), -1, dtype=torch.uint8, device="cuda")
+    out = torch.full((ql["M"], ql["H"]), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    a, _, _, info = run_quantized(ql, ws=ws, out=out)
+    assert info["variant"] == moe.MOE_VARIANT_TILED_QUANT
+    a = a.clone()
+    b, _, _, _ = run_quantized(ql, ws=ws)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check_quantized(ql, n_tokens=16, ws=ws)
 
 
 def test_quantized_streaming_poisoned_workspace_repeatable():
