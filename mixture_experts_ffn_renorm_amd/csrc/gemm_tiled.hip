@@ -78,7 +78,11 @@ namespace {
 constexpr int kBK = 64;          // k elements per stage = 128 bytes per row
 constexpr int kWaves = 8;
 constexpr int kRowBytes = kBK * 2;
-constexpr int kMeta = 5;         // tile metadata buffers (pair ids, expert)
+// Tile metadata buffers (pair ids, expert).  Tile i + 3's copies start when
+// the copy sources of tile i are set up, up to three stages before tile i's
+// first stage; the buffer they overwrite, tile i - 4's, has had its last
+// stage (at most four stages before) and epilogue by then.
+constexpr int kMeta = 7;
 
 // Tile shape per block size BM: 256 weight rows x BM pairs, MFMA waves in a
 // 4 (features, 64 rows each) x 2 (pair halves) layout.  With kPC four more
@@ -151,7 +155,7 @@ struct TileParams {
 // QB = 4 or 8: the weights are group-quantized codes (copy-wave tiles,
 // BM = 128 only); see the quantized ring below.
 template <int BM, bool kGemm1, bool kMX, bool kPC = false, int QB = 0>
-__global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_tiled_kernel(
+__global__ __launch_bounds__((QB > 0 ? 1024 : TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_tiled_kernel(
     const TileParams prm) {
   using C = TileCfg<BM, kMX, kPC>;
   static_assert(QB == 0 || (kPC && !kMX && BM == 128), "quantized tiles: copy waves, 128 pairs");
@@ -159,16 +163,18 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   constexpr int kStages = C::kStages;
   constexpr int kBN = C::kBN;
   constexpr int kHalf = kBN / 2;   // GEMM 1: gate rows, then as many up rows
-  // Quantized ring (QB > 0): A slots hold the stage's widened bf16 weight
-  // rows, B slots the gathered pair rows, code slots the stage's packed codes
-  // (kBN rows x 64 * QB / 8 bytes) and scale slots one 32-bit word of the
-  // scales, then of the biases, per weight row (the aligned word holding the
-  // stage's group value).
+  // Quantized ring (QB > 0): two A slots hold a stage's widened bf16 weight
+  // rows, kQXD + 1 B slots the gathered pair rows, three code slots the
+  // stage's packed codes (kBN rows x 64 * QB / 8 bytes) and three scale
+  // slots one 32-bit word of the scales, then of the biases, per weight row.
   constexpr int kQASlot = kBN * kRowBytes;                      // 32 KB
   constexpr int kQBSlot = BM * kRowBytes;                       // 16 KB
   constexpr int kQCB = kBK * (QB > 0 ? QB : 8) / 8;             // code bytes per row and stage
   constexpr int kQCSlot = kBN * kQCB;                           // 8 / 16 KB
   constexpr int kQSSlot = kBN * 4 * 2;                          // 2 KB
+  // pair rows are copied kQXD stages ahead into kQXD + 1 B slots (8 bits:
+  // one, so that three 16 KB code slots fit in LDS)
+  constexpr int kQXD = QB == 8 ? 1 : 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ __attribute__((aligned(16))) int s_pair[kMeta][BM];
   __shared__ int s_exp[kMeta];
@@ -190,8 +196,10 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lrow = lane >> 3, lpos = lane & 7;
   // copy wave index (kPC: waves kWaves.. copy, waves 0..kWaves-1 multiply)
-  const bool copier = !kPC || wv >= kWaves;
-  const int cw = kPC ? wv - kWaves : wv;
+  // QB > 0: waves kWaves + 4 .. kWaves + 7 widen the quantized weights
+  const bool widener = QB > 0 && wv >= kWaves + 4;
+  const bool copier = (!kPC || wv >= kWaves) && !widener;
+  const int cw = kPC ? wv - kWaves - (widener ? 4 : 0) : wv;
 
   // ---- metadata copies of tile i into buffer i % kMeta ----
   auto issue_meta = [&](int i) {
@@ -216,8 +224,24 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
   const uint8_t* ssrc[C::kScaleCopies > 0 ? C::kScaleCopies : 1];
   int sstep[C::kScaleCopies > 0 ? C::kScaleCopies : 1];
 
+  // Point the pair-row copy sources at tile i (its metadata is in LDS).
+  auto setup_x = [&](int i) {
+    const int buf = i % kMeta;
+#pragma unroll
+    for (int gi = 0; gi < C::kXGroups; ++gi) {
+      const int R = (cw + C::kCopyWaves * gi) * 8 + lrow;
+      const int p = s_pair[buf][R];
+      const uint16_t* row = nullptr;
+      if (p < P)
+        row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * K    // K: row length in
+                     : prm.a_src + (size_t)p * K;                 // 2-byte units
+      xsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
+      xstep[gi] = row != nullptr ? kBK : 0;
+    }
+  };
+
   // Point the copy sources at tile i (its metadata is in LDS), and start the
-  // metadata copies of tile i + 2.
+  // metadata copies of tile i + 3.
   auto setup = [&](int i) {
     const int buf = i % kMeta;
     const int j = j0 + i * nslots;
@@ -238,17 +262,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       wsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
       wstep[gi] = row != nullptr ? kBK : 0;
     }
-#pragma unroll
-    for (int gi = 0; gi < C::kXGroups; ++gi) {
-      const int R = (cw + C::kCopyWaves * gi) * 8 + lrow;
-      const int p = s_pair[buf][R];
-      const uint16_t* row = nullptr;
-      if (p < P)
-        row = kGemm1 ? prm.a_src + (size_t)(p / prm.top_k) * K    // K: row length in
-                     : prm.a_src + (size_t)p * K;                 // 2-byte units
-      xsrc[gi] = row != nullptr ? row + (lpos ^ swz(R)) * 8 : zero;
-      xstep[gi] = row != nullptr ? kBK : 0;
-    }
+    setup_x(i);
 #pragma unroll
     for (int h = 0; h < C::kScaleCopies; ++h) {
       const int R = (cw + C::kCopyWaves * h) * 64 + lane, nb = Ke / 32;
@@ -270,7 +284,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       ssrc[h] = srow != nullptr ? srow : reinterpret_cast<const uint8_t*>(kZeroPage);
       sstep[h] = srow != nullptr ? 4 : 0;
     }
-    issue_meta(i + 2);
+    issue_meta(i + 3);
   };
 
   int is_i = 0, is_kt = 0, is_slot = 0;
@@ -337,9 +351,10 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: metadata of tiles 0 and 1, then the first kStages-1 stages ----
+  // ---- prologue: metadata of tiles 0 to 2, then the first kStages-1 stages ----
   issue_meta(0);
   issue_meta(1);
+  issue_meta(2);
   wait_vmem<0>();
   __syncthreads();
 
@@ -417,9 +432,9 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
       act1 = __ballot(v1) != 0ull;
     }
     if constexpr (QB > 0) {
-      // quantized ring: A (widened weights) in two slots, B in three
+      // quantized ring: A (widened weights) in two slots, B in kQXD + 1
       const uint8_t* sa = ring + (c_g & 1) * kQASlot;
-      const uint8_t* sbb = ring + 2 * kQASlot + (c_g % 3) * kQBSlot;
+      const uint8_t* sbb = ring + 2 * kQASlot + (c_g % (kQXD + 1)) * kQBSlot;
       if (act0 || act1) compute(sa, sbb);
     } else {
       const uint8_t* sb = ring + c_slot * C::kStageBytes;
@@ -518,90 +533,152 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
     }
   };
 
-  // ---- quantized weights (QB > 0): the copy waves' loop ----
-  // Per stage g (64 k of tile g / nk): DMA of the stage's codes, the scale
-  // and bias words of its 256 weight rows and the gathered pair rows; once
-  // they have landed, each copy lane widens one weight row, w = s q + b
-  // rounded to bf16, into the stage's A slot in the layout the copies of
-  // bf16 weights give (chunk c of row R at slot c ^ swz(R)).  The A rows of
-  // stage g + 1 are widened while the MFMA waves multiply stage g.
+  // ---- quantized weights (QB > 0): copy waves and widen waves ----
+  // Copy waves DMA stage h's codes (and, at the start of a scale block, one
+  // aligned 32-bit word of the scales and one of the biases per weight row)
+  // three stages ahead, and its gathered pair rows kQXD stages ahead, and
+  // wait for them to land before the barriers: the codes of stage h by
+  // barrier h - 1, the pair rows by barrier h.  Between barriers h - 1 and h
+  // each lane of the widen waves widens one weight row of stage h, w = s q + b
+  // rounded to bf16, into the stage's A slot in the layout the copies of bf16
+  // weights give (chunk c of row R at slot c ^ swz(R)), while the MFMA waves
+  // multiply stage h - 1.  Separate waves, so copies that stall at issue
+  // never delay the widening.  A scale block is two stages when the group
+  // count per row is even (every row's word then starts at an even group),
+  // else one stage, with the half picked per row.  Codes use the default
+  // cache policy: a 128-byte line of codes serves 128 / kQCB stages.
+  [[maybe_unused]] constexpr int kQI = kQCSlot / 1024 / C::kCopyWaves;   // code copies per wave and stage
+  [[maybe_unused]] constexpr int kQRows = 1024 / kQCB;                  // code rows per copy
+  [[maybe_unused]] constexpr int kQChunks = kQCB / 16;                  // 16-byte chunks per code row and stage
+  uint8_t* const qa = ring;                                             // 2 A slots
+  uint8_t* const qb = ring + 2 * kQASlot;                               // kQXD + 1 B slots
+  uint8_t* const qc = qb + (kQXD + 1) * kQBSlot;                        // 3 code slots
+  uint8_t* const qs = qc + 3 * kQCSlot;                                 // 3 scale slots
+  const int ng = Ke / 64;
+  const int sb = (ng & 1) == 0 ? 2 : 1;                                 // stages per scale block
+  const int R = cw * 64 + lane;            // the weight row whose codes and words this lane moves
+  // global weight row of tile row r of tile i (or -1 past the weights)
+  auto wrow = [&](int i, int r) -> long long {
+    const int j = j0 + i * nslots;
+    const int nt = j - (j / ntn) * ntn;
+    const int e = s_exp[i % kMeta];
+    if (kGemm1) {
+      const int f = nt * kHalf + (r % kHalf);
+      return f < prm.I ? (long long)e * 2 * prm.I + (r < kHalf ? f : prm.I + f) : -1;
+    }
+    const int h = nt * kBN + r;
+    return h < prm.H ? (long long)e * prm.H + h : -1;
+  };
+
   auto quant_copier = [&]() {
     if constexpr (QB > 0) {
-      constexpr int kQI = kQCSlot / 1024 / C::kCopyWaves;   // code copies per wave and stage
-      constexpr int kQRows = 1024 / kQCB;                  // code rows per copy
-      constexpr int kQChunks = kQCB / 16;                  // 16-byte chunks per code row and stage
-      constexpr int kQC = kQI + C::kXGroups + 2;           // copies per wave and stage
-      uint8_t* const qa = ring;                            // 2 A slots
-      uint8_t* const qb = ring + 2 * kQASlot;              // 3 B slots
-      uint8_t* const qc = qb + 3 * kQBSlot;                // 2 code slots
-      uint8_t* const qs = qc + 2 * kQCSlot;                // 2 scale slots
+      constexpr int kX = C::kXGroups;                      // pair-row copies per wave and stage
       const int rowq = Ke * QB / 8;                        // code bytes per weight row
-      const int ng = Ke / 64;
-      const int R = cw * 64 + lane;                        // the weight row this lane widens
-      // global weight row of tile row r (or -1 past the weights)
-      auto wrow = [&](int nt, int e, int r) -> long long {
-        if (kGemm1) {
-          const int f = nt * kHalf + (r % kHalf);
-          return f < prm.I ? (long long)e * 2 * prm.I + (r < kHalf ? f : prm.I + f) : -1;
-        }
-        const int h = nt * kBN + r;
-        return h < prm.H ? (long long)e * prm.H + h : -1;
-      };
       const uint8_t* csrc[kQI];
-      const uint8_t* ssrc = nullptr;
-      const uint8_t* bsrc = nullptr;
       long long srow = -1;                                 // this lane's scale row (R)
-      int par0 = 0, par1 = 0;                              // half of the scale word, per code slot
-      int q_i = 0, q_kt = 0;
-      auto qissue = [&](int g) {
+      int q_i = 0, q_kt = 0, q_h = 0, nsb = 0, x_h = 0, x_i = 0, x_kt = 0;
+      // Codes (and the scale block's words) of the next stage; returns the
+      // number of memory operations (0 past the last stage).
+      auto issue_codes = [&]() -> int {
+        if (q_h >= G) return 0;
         if (q_kt == 0) {
-          setup(q_i);                                      // pair-row sources, metadata
-          const int buf = q_i % kMeta;
-          const int j = j0 + q_i * nslots;
-          const int nt = j - (j / ntn) * ntn;
-          const int e = s_exp[buf];
+          issue_meta(q_i + 3);
 #pragma unroll
           for (int q = 0; q < kQI; ++q) {
             const int r = (cw * kQI + q) * kQRows + lane / kQChunks;
-            const long long wr = wrow(nt, e, r);
+            const long long wr = wrow(q_i, r);
             csrc[q] = wr >= 0 ? prm.wq + wr * rowq + (lane % kQChunks) * 16 : nullptr;
           }
-          srow = wrow(nt, e, R);
-          ssrc = srow >= 0 ? prm.wsc : nullptr;
-          bsrc = srow >= 0 ? prm.wbi : nullptr;
+          srow = wrow(q_i, R);
         }
-        const int kt = q_kt;
+        const int kt = q_kt, h = q_h++;
         if (++q_kt == nk) { q_kt = 0; ++q_i; }
-        uint8_t* cdst = qc + (g & 1) * kQCSlot;
+        uint8_t* cdst = qc + (h % 3) * kQCSlot;
 #pragma unroll
         for (int q = 0; q < kQI; ++q)
-          load_lds16<kNonTemporal>(csrc[q] != nullptr ? (const void*)(csrc[q] + kt * kQCB)
-                                                      : (const void*)kZeroPage,
-                                   cdst + (cw * kQI + q) * 1024);
-        uint8_t* bdst = qb + (g % 3) * kQBSlot;
+          load_lds16(csrc[q] != nullptr ? (const void*)(csrc[q] + kt * kQCB)
+                                        : (const void*)kZeroPage,
+                     cdst + (cw * kQI + q) * 1024);
+        if (kt % sb != 0) return kQI;
+        // the aligned word holding group kt of row R (sb = 2: groups kt, kt + 1)
+        const long long el = srow >= 0 ? srow * ng + kt : 0;
+        uint8_t* sdst = qs + (nsb++ % 3) * kQSSlot;
+        load_lds4(srow >= 0 ? (const void*)(prm.wsc + (el & ~1ll) * 2) : (const void*)kZeroPage,
+                  sdst + cw * 256);
+        load_lds4(srow >= 0 ? (const void*)(prm.wbi + (el & ~1ll) * 2) : (const void*)kZeroPage,
+                  sdst + 1024 + cw * 256);
+        return kQI + 2;
+      };
+      // Pair rows of the next stage; returns the operation count.
+      auto issue_rows = [&]() -> int {
+        if (x_h >= G) return 0;
+        if (x_kt == 0) setup_x(x_i);
+        if (++x_kt == nk) { x_kt = 0; ++x_i; }
+        uint8_t* bdst = qb + (x_h++ % (kQXD + 1)) * kQBSlot;
 #pragma unroll
-        for (int gi = 0; gi < C::kXGroups; ++gi) {
+        for (int gi = 0; gi < kX; ++gi) {
           load_lds16(xsrc[gi], bdst + (cw + C::kCopyWaves * gi) * 8 * kRowBytes);
           xsrc[gi] += xstep[gi];
         }
-        // the aligned 32-bit word that holds group kt of row R, and its half
-        const long long word = srow >= 0 ? ((srow * ng + kt) & ~1ll) : 0;
-        const int par = srow >= 0 ? (int)((srow * ng + kt) & 1) : 0;
-        if (g & 1) par1 = par; else par0 = par;
-        uint8_t* sdst = qs + (g & 1) * kQSSlot;
-        load_lds4(ssrc != nullptr ? (const void*)(ssrc + word * 2) : (const void*)kZeroPage,
-                  sdst + cw * 256);
-        load_lds4(bsrc != nullptr ? (const void*)(bsrc + word * 2) : (const void*)kZeroPage,
-                  sdst + 1024 + cw * 256);
+        return kX;
       };
-      auto widen = [&](int g) {
-        const uint8_t* cr = qc + (g & 1) * kQCSlot + R * kQCB;
-        const uint8_t* ss = qs + (g & 1) * kQSSlot;
+      // at most n memory operations of this wave pending; n is one of the
+      // sizes a run of the latest copies can have (else: wait for all)
+      auto wait_n = [&](int n) {
+        if (n == 0) wait_vmem<0>();
+        else if (n == kX) wait_vmem<kX>();
+        else if (n == kQI) wait_vmem<kQI>();
+        else if (n == kQI + 2) wait_vmem<kQI + 2>();
+        else if (n == kX + kQI) wait_vmem<kX + kQI>();
+        else if (n == kX + kQI + 2) wait_vmem<kX + kQI + 2>();
+        else if (n == 2 * kX + 2 * kQI) wait_vmem<2 * kX + 2 * kQI>();
+        else if (n == 2 * kX + 2 * kQI + 2) wait_vmem<2 * kX + 2 * kQI + 2>();
+        else if (n == 2 * kX + 2 * kQI + 4) wait_vmem<2 * kX + 2 * kQI + 4>();
+        else wait_vmem<0>();
+      };
+      // Batch b = rows(b + kQXD), codes(b + 3); batches -2 and -1 after
+      // codes(0) before the first barrier, batch b >= 0 after barrier b.
+      // Before barrier b + 1, codes(b + 2) (batch b - 1) and rows(b + 1)
+      // (batch b + 1 - kQXD) must have landed: all but the last batch's
+      // operations (kQXD = 2), or all but its codes' (kQXD = 1).
+      issue_codes();
+      const int r2 = kQXD == 2 ? issue_rows() : 0;   // batch -2
+      const int c2 = issue_codes();
+      int r1 = issue_rows();                         // batch -1
+      int c1 = issue_codes();
+      wait_n(r2 + c2 + r1 + c1);                     // codes(0)
+      barrier_nofence();                             // barrier -1
+      wait_n((kQXD == 2 ? r1 : 0) + c1);             // codes(1), rows(0)
+      wait_lgkm0();
+      barrier_nofence();                             // barrier 0
+      for (int g = 0; g + 1 < G; ++g) {
+        r1 = issue_rows();                           // batch g
+        c1 = issue_codes();
+        wait_n((kQXD == 2 ? r1 : 0) + c1);           // codes(g + 2), rows(g + 1)
+        barrier_nofence();                           // barrier g + 1
+      }
+      wait_vmem<0>();                                // no copy outlives the wave
+    }
+  };
+
+  auto quant_widener = [&]() {
+    if constexpr (QB > 0) {
+      int w_i = 0, w_kt = 0, wsb = -1;
+      long long wr = -1;                                   // global row of R in the current tile
+      barrier_nofence();                                   // barrier -1: codes(0) are in LDS
+      for (int g = 0; g < G; ++g) {
+        const int kt = w_kt;
+        if (kt == 0) wr = wrow(w_i, R);
+        if (++w_kt == nk) { w_kt = 0; ++w_i; }
+        if (kt % sb == 0) ++wsb;
+        const uint8_t* cr = qc + (g % 3) * kQCSlot + R * kQCB;
+        const uint8_t* ss = qs + (wsb % 3) * kQSSlot;
         const uint32_t swd = *reinterpret_cast<const uint32_t*>(ss + R * 4);
         const uint32_t bwd = *reinterpret_cast<const uint32_t*>(ss + 1024 + R * 4);
-        const int par = (g & 1) ? par1 : par0;
-        const float sc = par ? bf16_hi(swd) : bf16_lo(swd);
-        const float bi = par ? bf16_hi(bwd) : bf16_lo(bwd);
+        // the half of the word holding group kt (rows past the weights read 0)
+        const int half = sb == 2 ? (kt & 1) : (int)((wr >= 0 ? wr * ng + kt : 0) & 1);
+        const float sc = half ? bf16_hi(swd) : bf16_lo(swd);
+        const float bi = half ? bf16_hi(bwd) : bf16_lo(bwd);
         uint8_t* arow = qa + (g & 1) * kQASlot + R * kRowBytes;
         u32x4 cw4[kQCB / 16];
 #pragma unroll
@@ -610,9 +687,12 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
         for (int c = 0; c < 8; ++c) {      // 8 values a chunk, 8 chunks of 64 k
           float v[8];
           if constexpr (QB == 4) {
-            // nibble 2j is byte j of lo, nibble 2j + 1 byte j of hi
-            const uint32_t w = cw4[c >> 2][c & 3];
-            const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+            // nibble 2j is byte j of lo, nibble 2j + 1 byte j of hi; the
+            // empty asm hides that their bytes are below 16, so the byte
+            // conversions (one instruction each) stay
+            uint32_t lo = cw4[c >> 2][c & 3] & 0x0F0F0F0Fu;
+            uint32_t hi = (cw4[c >> 2][c & 3] >> 4) & 0x0F0F0F0Fu;
+            asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               v[2 * k] = (float)((lo >> (8 * k)) & 255u);
@@ -632,20 +712,8 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
             o[k] = pack_bf16x2(__builtin_fmaf(sc, v[2 * k], bi), __builtin_fmaf(sc, v[2 * k + 1], bi));
           *reinterpret_cast<u32x4*>(arow + ((c ^ swz(R)) << 4)) = o;
         }
-      };
-      qissue(0);
-      if (G > 1) qissue(1);
-      if (G > 1) wait_vmem<kQC>(); else wait_vmem<0>();
-      widen(0);
-      for (int g = 0; g < G; ++g) {
         wait_lgkm0();        // this lane's A rows of stage g are in LDS
-        barrier_nofence();   // stage g is complete; stage g-1 has been consumed
-        if (g + 2 < G) qissue(g + 2);
-        if (g + 1 < G) {
-          // stage g + 1's copies have landed once at most stage g + 2's are pending
-          if (g + 2 < G) wait_vmem<kQC>(); else wait_vmem<0>();
-          widen(g + 1);
-        }
+        barrier_nofence();   // barrier g
       }
     }
   };
@@ -655,6 +723,8 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
     // so neither keeps the other's registers live.
     if (copier && QB > 0) {
       quant_copier();
+    } else if (widener) {
+      quant_widener();
     } else if (copier) {
 #pragma unroll
       for (int g = 0; g < kStages - 1; ++g)
@@ -666,6 +736,7 @@ __global__ __launch_bounds__((TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_ti
         if (g + kStages - 1 < G) issue_stage();
       }
     } else {
+      if (QB > 0) barrier_nofence();   // barrier -1 (the widen waves start stage 0)
       for (int g = 0; g < G; ++g) {
         barrier_nofence();
         consume();
@@ -747,16 +818,16 @@ hipError_t launch_tiled(const moe_host::GemmArgs& a, hipStream_t s, uint16_t* ou
   const long long tiles = (long long)a.max_blocks * prm.ntn;
   long long grid = std::min<long long>(tiles, moe_host::device_cu_count());
   grid = std::max<long long>(8, (grid + 7) / 8 * 8);
-  // quantized ring: 2 A slots, 3 B slots, 2 code slots, 2 scale slots
-  const size_t lds = QB > 0 ? (size_t)2 * kBN * kRowBytes + 3 * BM * kRowBytes +
-                                  2 * kBN * (kBK * QB / 8) + 2 * kBN * 8
+  // quantized ring: 2 A slots, 3 (8 bits: 2) B slots, 3 code slots, 3 scale slots
+  const size_t lds = QB > 0 ? (size_t)2 * kBN * kRowBytes + (QB == 8 ? 2 : 3) * BM * kRowBytes +
+                                  3 * kBN * (kBK * QB / 8) + 3 * kBN * 8
                             : C::kRingBytes;
   static bool lds_set[moe_host::kMaxDevices] = {};
   const hipError_t err = moe_host::ensure_dynamic_lds(
       reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, kGemm1, kMX, kPC, QB>), (int)lds, lds_set);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_tiled_kernel<BM, kGemm1, kMX, kPC, QB>), dim3((unsigned)grid),
-                     dim3(C::kThreadsT), lds, s, prm);
+                     dim3(QB > 0 ? 1024 : C::kThreadsT), lds, s, prm);
   return hipGetLastError();
 }
 
