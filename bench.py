@@ -17,7 +17,9 @@ Prints ONE JSON line:
   kernels_us       mean duration of every per-step call (events)
   prefill          the Zipf-routed Qwen3-shaped layer at 4096 tokens timed
                    the same way, with its own roofline (GEMM 1 flops / its
-                   mean launch time against the bf16 MFMA peak)
+                   mean launch time against the bf16 MFMA peak), and the
+                   same batch on 4- and 8-bit group-quantized experts
+                   (expert flops / layer time against the bf16 MFMA peak)
   mxfp8            context: moe_forward_mxfp8 (MXFP8 experts and GEMM inputs)
                    on the same shape and batch, the L layers drawn as MXFP8
                    (mxfp8_M1: the same at one token, the per-pair GEMVs)
@@ -196,6 +198,7 @@ def main():
         pname, pM = PREFILL_WORKLOAD
         pm = measure_layer(wl.WORKLOADS[pname], pM, max(1, min(L, args.prefill_layers)),
                            args.steps, args.warmup, dev, stream)
+        px = pm["_x"]
         for key in ("_layers", "_x", "_ws", "_info"):
             pm.pop(key)
         result["prefill"] = {"workload": pname, "M": pM, "ms_per_layer": pm["ms_per_layer"],
@@ -204,6 +207,18 @@ def main():
                              "hbm_frac": pm["layer"]["hbm_frac"], "layer": pm["layer"],
                              "kernels_us": pm["kernels_us"], "roofline": pm["roofline"],
                              "config": pm["config"]}
+        torch.cuda.empty_cache()
+        if not args.no_quant:
+            # the same batch on 4- and 8-bit group-quantized experts (tiles
+            # with the codes widened in LDS), MFMA fraction as the bf16 layer's
+            pshape = wl.WORKLOADS[pname]
+            pq = quantized_figures(pshape, 2, px, dev, max(5, min(args.steps, 20)),
+                                   [(4, pM), (8, pM)])
+            for v in pq.values():
+                fl = 6.0 * pshape.H * pshape.I * pM * pshape.top_k
+                v["mfma_frac"] = round(fl / (v["us_per_layer"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            result["prefill"]["quantized"] = pq
+        del px
         torch.cuda.empty_cache()
 
     # ---- decode sweep (same shape, smaller batches) ----

@@ -420,13 +420,15 @@ int moe_forward_quantized(const uint16_t* x, const uint16_t* w_router, const flo
   // per-pair GEMVs up to E/2 pairs, weight-streaming GEMMs over block_m 16
   // index lists (per-pair GEMVs instead for shapes the streaming kernels do
   // not take), the copy-wave tiles with the codes widened in LDS over
-  // block_m 128 lists where the bf16 layer runs 128- or 256-pair tiles.
-  // Measured on the Qwen3 shape (E = 128, top_k = 8): 8 tokens 63 / 71 us
-  // per-pair against 69 / 81 streaming (4 / 8 bits), 16 tokens 103 / 129
-  // against 84 / 102.
+  // block_m 128 lists where the bf16 layer runs tiles (more than 8 pairs per
+  // expert).  Measured on the Qwen3 shape (E = 128, top_k = 8; us, 4 / 8
+  // bits): 8 tokens 63 / 71 per-pair against 69 / 81 streaming, 16 tokens
+  // 103 / 129 against 84 / 102; 128 tokens 102 / 126 streaming against
+  // 132 / 145 tiled, 256 tokens 155 / 191 against 152 / 158, 512 tokens
+  // 245 / 318 against 198 / 209.
   int B = 1;
   if ((long long)M * top_k * 2 > E) {
-    if (moe_pick_block_m(M, E, top_k) >= 128) B = 128;
+    if (moe_pick_block_m(M, E, top_k) >= 64) B = 128;
     else if (qgemm_stream_shapes_ok(H, I)) B = 16;
   }
   const bool per_pair = B == 1;

@@ -176,7 +176,9 @@ def test_forward_quantized_argument_checks(bits, group, H, I, M, status):
 @pytest.mark.parametrize("M,H,I,variant,launches", [
     (1, 2048, 768, "pair", 4),          # M*top_k*4 <= E: per-pair GEMVs
     (64, 2048, 768, "stream", 5),       # router, fused top-k + lists, GEMM 1, GEMM 2, sum
-    (512, 2048, 768, "stream", 7),      # 4096 pairs: top-k, count, scatter launches
+    (128, 2048, 768, "stream", 5),      # 8 pairs per expert: still streaming
+    (256, 2048, 768, "tiled", 5),       # 16 pairs per expert: tiles
+    (512, 4096, 768, "tiled", 7),       # 4096 pairs: top-k, count, scatter launches
     (64, 2048 + 64, 768, "pair", 4),    # H % 128 != 0: per-pair GEMVs at any M
     (64, 2048, 768 + 64, "pair", 4),
     (1024, 2048, 768, "tiled", 7),      # 64 pairs per expert: bf16 tiles widened in LDS
