@@ -285,8 +285,8 @@ def main():
                                                max(5, min(args.steps, 50)))
 
     # ---- group-quantized expert weights at small batches (context) ----
-    if not args.no_quant and shape.H % 64 == 0 and shape.I % 64 == 0 and M <= 64:
-        sizes = [tuple(int(v) for v in p.split(":")) for p in args.quant_sizes.split(",") if p]
+    sizes = [tuple(int(v) for v in p.split(":")) for p in args.quant_sizes.split(",") if p]
+    if not args.no_quant and sizes and shape.H % 64 == 0 and shape.I % 64 == 0 and M <= 64:
         result["quantized"] = quantized_figures(shape, L, x, dev, max(10, min(args.steps, 50)),
                                                 sizes)
 
