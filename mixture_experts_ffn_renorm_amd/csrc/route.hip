@@ -143,14 +143,24 @@ __global__ __launch_bounds__(256) void route_logits_gemv_kernel(
 // Router logits for large batches: LDS-tiled MFMA GEMM over a tile of BT
 // tokens (32 or 64) x EX experts (32, 64 or 128), 4 waves (2 expert halves
 // x 2 token halves, each EX/2 experts x BT/2 tokens).  K goes through LDS in stages of
-// 64 elements, three deep, copied with global_load_lds_dwordx4; rows are
-// 128 bytes with chunk c of row R at slot c ^ ((R >> 1) & 7) (conflict-free
-// operand reads).  Expert rows and token rows past the ends, and the K
-// tail, copy a zeroed page.  Each W_r tile is read by M/BT workgroups and
-// each token row by E/EX, all other reuse comes from LDS; the host picks the
-// tile that moves the fewest bytes per CU.
+// KS sub-tiles of 64 elements, three stages deep, copied with
+// global_load_lds_dwordx4; a sub-tile's rows are 128 bytes with chunk c of
+// row R at slot c ^ ((R >> 1) & 7) (conflict-free operand reads).  Expert
+// rows and token rows past the ends, and the K tail, copy a zeroed page.
+// Each W_r tile is read by M/BT workgroups and each token row by E/EX, all
+// other reuse comes from LDS; the host picks the tile that moves the fewest
+// bytes per CU.  The grid is about one workgroup per CU, so a stage holds as
+// many sub-tiles as 144 KB of LDS allows: fewer, larger stages keep more
+// bytes in flight per CU than 64-element stages.
 constexpr int kRtBK = 64;
 constexpr int kRtStages = 3;
+constexpr int kRtMaxLds = 144 * 1024;
+template <int BT, int EX>
+struct RtCfg {
+  static constexpr int kRows = EX + BT;
+  static constexpr int KS = 3 * 4 * kRows * 128 <= kRtMaxLds ? 4 : 3 * 2 * kRows * 128 <= kRtMaxLds ? 2 : 1;
+  static constexpr int kLds = kRtStages * KS * kRows * 128;
+};
 
 __device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
 
@@ -160,8 +170,10 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
     const float* __restrict__ bias, int M, int H, int E, float* __restrict__ logits,
     float* __restrict__ zero_ptr, size_t zero_words) {
   constexpr int kRows = EX + BT;
-  constexpr int kStageBytes = kRows * 128;
-  constexpr int kCopies = kRows / 8 / 4;     // 1 KB copies per wave per stage
+  constexpr int KS = RtCfg<BT, EX>::KS;      // 64-element sub-tiles per stage
+  constexpr int kSubBytes = kRows * 128;
+  constexpr int kStageBytes = KS * kSubBytes;
+  constexpr int kCopies = kRows / 8 / 4;     // 1 KB copies per wave per sub-tile
   constexpr int NTA = EX / 32;               // 16-expert MFMA tiles per wave
   constexpr int NTB = BT / 32;               // 16-token MFMA tiles per wave
   static_assert(kCopies * 32 == kRows, "copies cover the stage");
@@ -186,16 +198,20 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
     }
     src[c] = row != nullptr ? row + (lpos ^ rt_swz(R)) * 8 : nullptr;
   }
-  const int nk = ceil_div(H, kRtBK);
+  const int nk = ceil_div(H, kRtBK * KS);
   auto issue = [&](int kt) {
     uint8_t* sb = lds + (kt % kRtStages) * kStageBytes;
-    const int kend = H - kt * kRtBK;
 #pragma unroll
-    for (int c = 0; c < kCopies; ++c) {
-      const int R = (wv * kCopies + c) * 8 + lrow;
-      const uint16_t* p = (src[c] != nullptr && (lpos ^ rt_swz(R)) * 8 < kend)
-                              ? src[c] + kt * kRtBK : zero;
-      load_lds16(p, sb + (wv * kCopies + c) * 1024);
+    for (int u = 0; u < KS; ++u) {
+      const int k0 = (kt * KS + u) * kRtBK;
+      const int kend = H - k0;   // valid elements of this sub-tile (may be <= 0)
+#pragma unroll
+      for (int c = 0; c < kCopies; ++c) {
+        const int R = (wv * kCopies + c) * 8 + lrow;
+        const uint16_t* p = (src[c] != nullptr && (lpos ^ rt_swz(R)) * 8 < kend)
+                                ? src[c] + k0 : zero;
+        load_lds16(p, sb + u * kSubBytes + (wv * kCopies + c) * 1024);
+      }
     }
   };
 
@@ -217,21 +233,24 @@ __global__ __launch_bounds__(256) void route_logits_tiled_kernel(
   issue(0);
   if (nk > 1) issue(1);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vmem<kCopies>(); else wait_vmem<0>();
+    if (kt + 1 < nk) wait_vmem<KS * kCopies>(); else wait_vmem<0>();
     barrier_nofence();
     if (kt + 2 < nk) issue(kt + 2);
-    const uint8_t* sb = lds + (kt % kRtStages) * kStageBytes;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 af[NTA], bfr[NTB];
+    for (int u = 0; u < KS; ++u) {
+      const uint8_t* sb = lds + (kt % kRtStages) * kStageBytes + u * kSubBytes;
 #pragma unroll
-      for (int i = 0; i < NTA; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + i * 16 * 128);
+      for (int s = 0; s < 2; ++s) {
+        u32x4 af[NTA], bfr[NTB];
 #pragma unroll
-      for (int j = 0; j < NTB; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] + j * 16 * 128);
+        for (int i = 0; i < NTA; ++i) af[i] = *reinterpret_cast<const u32x4*>(sb + abase[s] + i * 16 * 128);
 #pragma unroll
-      for (int i = 0; i < NTA; ++i)
+        for (int j = 0; j < NTB; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(sb + bbase[s] + j * 16 * 128);
 #pragma unroll
-        for (int j = 0; j < NTB; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int i = 0; i < NTA; ++i)
+#pragma unroll
+          for (int j = 0; j < NTB; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+      }
     }
   }
   // C: lane holds experts e0 + we + 16 i + 4 kg + q for token t0 + wt + 16 j + r16.
@@ -319,27 +338,24 @@ hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
         if (best < 0 || cost < best) { best = cost; best_bt = bt; best_ex = ex; }
       }
     dim3 grid(ceil_div_host(a.M, best_bt), ceil_div_host(a.E, best_ex));
-    const size_t lds = (size_t)kRtStages * (best_ex + best_bt) * 128;
-    auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, a.x, a.w_router, a.bias, a.M, a.H, a.E,
-                         a.logits, a.zero_ptr, a.zero_words);
+    hipError_t e = hipSuccess;
+    auto go = [&](auto kern, int lds, bool (&lds_set)[kMaxDevices]) {
+      // stages above the default limit of dynamic LDS
+      e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
+      if (e != hipSuccess) return;
+      hipLaunchKernelGGL(kern, grid, dim3(256), (size_t)lds, s, a.x, a.w_router, a.bias, a.M, a.H,
+                         a.E, a.logits, a.zero_ptr, a.zero_words);
     };
+    static bool set[6][kMaxDevices] = {};
     switch (best_bt * 1000 + best_ex) {
-      case 32032: go(route_logits_tiled_kernel<32, 32>); break;
-      case 32064: go(route_logits_tiled_kernel<32, 64>); break;
-      case 32128: go(route_logits_tiled_kernel<32, 128>); break;
-      case 64032: go(route_logits_tiled_kernel<64, 32>); break;
-      case 64064: go(route_logits_tiled_kernel<64, 64>); break;
-      default: {
-        // 72 KB of LDS: above the default limit of dynamic LDS
-        static bool lds_set[kMaxDevices] = {};
-        const hipError_t e = ensure_dynamic_lds(
-            reinterpret_cast<const void*>(&route_logits_tiled_kernel<64, 128>), (int)lds, lds_set);
-        if (e != hipSuccess) return e;
-        go(route_logits_tiled_kernel<64, 128>);
-        break;
-      }
+      case 32032: go(route_logits_tiled_kernel<32, 32>, RtCfg<32, 32>::kLds, set[0]); break;
+      case 32064: go(route_logits_tiled_kernel<32, 64>, RtCfg<32, 64>::kLds, set[1]); break;
+      case 32128: go(route_logits_tiled_kernel<32, 128>, RtCfg<32, 128>::kLds, set[2]); break;
+      case 64032: go(route_logits_tiled_kernel<64, 32>, RtCfg<64, 32>::kLds, set[3]); break;
+      case 64064: go(route_logits_tiled_kernel<64, 64>, RtCfg<64, 64>::kLds, set[4]); break;
+      default: go(route_logits_tiled_kernel<64, 128>, RtCfg<64, 128>::kLds, set[5]); break;
     }
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
