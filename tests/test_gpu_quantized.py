@@ -265,3 +265,53 @@ def test_quantized_poisoned_workspace_and_output():
     out = torch.full((3, ql["H"]), float("nan"), dtype=torch.bfloat16, device="cuda")
     got, _, _, _ = run_quantized(ql, ws=ws, out=out)
     assert torch.equal(got.view(torch.int16), ref_out.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,M,bits,over", [
+    ("qwen3_decode", 2, 4, {}),                                  # per-pair GEMVs
+    ("qwen3_decode", 16, 8, {}),                                 # streaming GEMMs
+    ("toy", 300, 4, dict(E=8, top_k=2, H=576, I=320)),           # tiles, one segment
+    ("toy", 1200, 8, dict(E=8, top_k=2, H=256, I=192)),          # tiles, multi-segment lists
+])
+def test_quantized_graph_replay_matches_eager(name, M, bits, over):
+    """moe_forward_quantized captured once into a HIP graph: every replay, with
+    other eager launches in between, gives the eager call's bits."""
+    import torch
+    seed = {"seed": 3400 + M + bits} if over else {}
+    ql = wl.make_quantized_layer(name, M, bits, **over, **seed)
+    moe = _moe()
+    k = ql["top_k"]
+    q = quant_to_device(ql)
+    wr = h.dev_bf16(ql["w_router"])
+    lb = None if ql.get("logit_bias") is None else h.dev_f32(ql["logit_bias"])
+    inputs = [h.dev_bf16(ql["x"])]
+    for r in (1, 2):   # other batches: the same rows permuted
+        perm = np.random.default_rng(100 + r).permutation(M)
+        inputs.append(h.dev_bf16(np.ascontiguousarray(ql["x"][perm])))
+    ws = moe.workspace(M, ql["E"], k, ql["H"], ql["I"])
+    eager_out = torch.empty((M, ql["H"]), dtype=torch.bfloat16, device="cuda")
+
+    def run(x, out):
+        return moe.moe_forward_quantized(x, wr, q, k, ql["renormalize"], logit_bias=lb,
+                                         out=out, ws=ws)[1]
+
+    refs = []
+    for xr in inputs:
+        run(xr, eager_out)
+        torch.cuda.synchronize()
+        refs.append(eager_out.clone())
+    x_static = inputs[0].clone()
+    out = torch.empty_like(eager_out)
+    run(x_static, out)                       # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        info = run(x_static, out)
+    print(f"quantized graph case {name} M={M} bits={bits} variant={info['variant']}", flush=True)
+    for r in range(3):
+        x_static.copy_(inputs[r])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), refs[r].view(torch.int16)), f"replay {r}"
+        run(inputs[(r + 1) % 3], eager_out)   # eager work between replays
+        torch.cuda.synchronize()
