@@ -204,6 +204,8 @@ TILED_CASES = [
     ("qwen3_prefill", 1024, 8, {}),
     ("qwen15", 1024, 4, {}),                                    # I = 1408: 22 k stages in GEMM 2
     ("wide256", 2048, 8, {}),                                   # 256 experts, I = 512
+    ("qwen3_prefill", 4096, 4, {}),                             # the prefill batch bench.py times
+    ("qwen3_prefill", 4096, 8, {}),
     ("toy", 200, 4, dict(E=8, top_k=2, H=576, I=320)),         # H, I % 64 only; N tails
     ("toy", 200, 8, dict(E=8, top_k=2, H=576, I=320)),
     ("toy", 300, 4, dict(E=4, top_k=1, H=64, I=64)),           # one k stage: one stage per tile
