@@ -223,6 +223,24 @@ def test_quantized_tiled(name, M, bits, over):
     check_quantized(ql, n_tokens=32)
 
 
+# Shapes drawn once (numpy seed 2026) among H, I multiples of 64 with more
+# than 8 pairs per expert: 1 to 23 k stages (odd and even group counts), N
+# tails, 1 to 64 experts, top_k 1 to 8, one- and multi-segment index lists.
+RANDOM_TILED = [
+    (553, 4, 64, 1, 64, 640), (1247, 8, 4, 2, 960, 384), (1288, 8, 60, 8, 1088, 192),
+    (1094, 8, 4, 2, 256, 960), (184, 8, 8, 4, 896, 768), (694, 4, 32, 8, 1024, 448),
+    (1281, 8, 4, 2, 256, 256), (1246, 4, 4, 2, 448, 640), (254, 4, 16, 2, 1472, 384),
+    (997, 4, 16, 4, 512, 448), (1435, 8, 64, 1, 1408, 896), (699, 8, 32, 4, 320, 384),
+]
+
+
+@pytest.mark.parametrize("M,bits,E,top_k,H,I", RANDOM_TILED)
+def test_quantized_tiled_random_shapes(M, bits, E, top_k, H, I):
+    ql = wl.make_quantized_layer("toy", M, bits, E=E, top_k=top_k, H=H, I=I, seed=3500 + M)
+    assert tiles(ql)
+    check_quantized(ql, n_tokens=24)
+
+
 def test_quantized_tiled_poisoned_workspace_repeatable():
     """Workspace and output filled with 0xFF bytes, then reused: identical
     outputs on the tiled path."""
