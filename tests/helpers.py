@@ -3,6 +3,8 @@ the comparison protocol against the CPU oracle."""
 
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 
 from oracle import moe_oracle as mo
@@ -103,3 +105,87 @@ def scatter_routing(M: int, toks: np.ndarray, ids: np.ndarray, wts: np.ndarray):
     full_ids[toks] = ids
     full_w[toks] = wts
     return full_ids, full_w
+
+
+# relative distance of an fp64 act value from a bf16 rounding midpoint below
+# which the GPU's fp32 sums (K terms, fp32 accumulation, fast exp) may round
+# it the other way
+ACT_ROUNDING_TOL = 2.0 ** -13
+
+
+def mx_ambiguous_act_choices(act64: np.ndarray):
+    """act values (float64, bf16-exact) of one pair for every combination of
+    the quantization decisions that could go either way: elements whose fp64
+    value lies within ACT_ROUNDING_TOL of a bf16 rounding midpoint and whose
+    E4M3 code or block scale changes on the other side of it.  None if more
+    than four such elements."""
+    bits = mo.round_to_bf16_via_f32(act64)
+    a = mo.widen_bf16(bits)
+    codes0, scales0 = mo.mx_quantize(a)
+    options = []
+    for i in range(a.size):
+        if (bits[i] & 0x7FFF) == 0:
+            continue
+        # the bf16 neighbour on the side of the fp64 value (bits -1 / +1 step
+        # the magnitude down / up)
+        toward_larger_mag = abs(act64[i]) > abs(a[i])
+        nb = int(bits[i]) + (1 if toward_larger_mag else -1)
+        if (nb & 0x7F80) == 0x7F80:
+            continue
+        nv = mo.widen_bf16(np.array([nb], dtype=np.uint16))[0]
+        if abs(act64[i] - 0.5 * (a[i] + nv)) > ACT_ROUNDING_TOL * abs(act64[i]):
+            continue
+        blk = i // mo.MX_BLOCK
+        sl = slice(blk * mo.MX_BLOCK, (blk + 1) * mo.MX_BLOCK)
+        alt = a[sl].copy()
+        alt[i - blk * mo.MX_BLOCK] = nv
+        c, sc = mo.mx_quantize(alt)
+        if not (np.array_equal(c, codes0[sl]) and sc[0] == scales0[blk]):
+            options.append((i, nv))
+    if len(options) > 4:
+        return None
+    out = []
+    for mask in range(1 << len(options)):
+        v = a.copy()
+        for bit, (i, val) in enumerate(options):
+            if mask >> bit & 1:
+                v[i] = val
+        out.append(v)
+    return out
+
+
+def mx_boundary_reference(lay, full_ids, full_w, toks, y, ref_y):
+    """ref_y with the rows of tokens over the max-abs bound replaced by the
+    closest oracle output among the act decisions one bf16 step could flip
+    (unchanged where no choice meets the bound)."""
+    bad = np.flatnonzero(np.abs(y - ref_y).max(axis=1) > MAX_ABS_REL * np.abs(ref_y).max())
+    if bad.size == 0:
+        return ref_y
+    I = lay["I"]
+    xq, xs = mo.mx_quantize(mo.widen_bf16(lay["x"][toks]))
+    X = mo.mx_dequantize(xq, xs)
+    ref = ref_y.copy()
+    bound = MAX_ABS_REL * np.abs(ref_y).max()
+    for r in bad:
+        per_pair = []
+        for j in range(lay["top_k"]):
+            e = full_ids[toks[r], j]
+            W13 = mo.mx_dequantize(lay["w13_codes"][e], lay["w13_scales"][e])
+            W2 = mo.mx_dequantize(lay["w2_codes"][e], lay["w2_scales"][e])
+            choices = mx_ambiguous_act_choices(mo.swiglu(X[r] @ W13.T, I))
+            if choices is None:
+                per_pair = None
+                break
+            per_pair.append([full_w[toks[r], j] * (mo.mx_dequantize(*mo.mx_quantize(c)) @ W2.T)
+                             for c in choices])
+        if per_pair is None:
+            continue
+        best, best_err = None, np.inf
+        for combo in itertools.product(*per_pair):
+            cand = np.sum(combo, axis=0)
+            err = np.abs(y[r] - cand).max()
+            if err < best_err:
+                best, best_err = cand, err
+        if best_err <= bound:
+            ref[r] = best
+    return ref

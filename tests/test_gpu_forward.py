@@ -268,3 +268,23 @@ def test_forward_long_k(long_k_layer, M, variant):
     want = {"pair": moe.MOE_VARIANT_PAIR_GEMV, "stream": moe.MOE_VARIANT_STREAM,
             "tiled": moe.MOE_VARIANT_TILED}[variant]
     assert info["variant"] == want
+
+
+# Tiled-path shapes drawn once (numpy seed 2027) with block_m 64, 128 and
+# 256: 1 to 23 k stages, N tails, 4 to 128 experts, top_k 1 to 8, one- and
+# multi-segment index lists; the last two have K tails (H and I multiples
+# of 8 only).
+RANDOM_TILED = [
+    (860, 60, 1, 256, 384), (1350, 4, 2, 768, 896), (379, 60, 4, 960, 320),
+    (276, 60, 4, 832, 128), (2172, 64, 1, 832, 384), (2884, 128, 4, 64, 832),
+    (1612, 128, 4, 576, 704), (2151, 8, 1, 896, 832), (2593, 128, 8, 896, 64),
+    (2389, 4, 1, 1472, 320), (900, 16, 2, 200, 136), (1500, 32, 4, 1000, 520),
+]
+
+
+@pytest.mark.parametrize("M,E,top_k,H,I", RANDOM_TILED)
+def test_forward_tiled_random_shapes(M, E, top_k, H, I):
+    moe = _moe()
+    assert moe.moe_pick_block_m(M, E, top_k) >= 64
+    lay = wl.make_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3600 + M)
+    check_forward(lay, n_tokens=32)

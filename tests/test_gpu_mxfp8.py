@@ -18,6 +18,13 @@ oracle's mx_quantize and forward_mxfp8.
   a poisoned workspace; weight codes span the whole finite E4M3 range.
   Outputs of every sampled token are compared against the oracle's MXFP8
   layer on the GPU's own ids.
+* act is quantized from its bf16 value, which the GPU forms from fp32 sums
+  and the oracle from fp64 ones; where an act element sits within one bf16
+  step of an E4M3 rounding boundary, or its block's largest magnitude within
+  one step of a power of two (the shared scale), either decision is correct.
+  A token whose output misses the bound is accepted only if the oracle's
+  layer with some choice of those decisions (at most four per pair) meets
+  it; the mean-relative error is then taken against that choice.
 """
 
 from __future__ import annotations
@@ -137,6 +144,7 @@ def check_mx(lay: dict, n_tokens: int = 48, seed: int = 0, **kw):
     full_ids, full_w = h.scatter_routing(lay["M"], toks, ids[toks], w_ref)
     ref_y, _, _ = mo.mx_layer_forward(lay, full_ids, full_w, toks)
     y = h.host_bf16_to_f64(out)[toks]
+    ref_y = h.mx_boundary_reference(lay, full_ids, full_w, toks, y, ref_y)
     h.assert_close_outputs(y, ref_y, "mxfp8 output")
     return out
 
@@ -189,3 +197,18 @@ def test_forward_mxfp8_poisoned_workspace():
     out = torch.full((70, 384), float("nan"), dtype=torch.bfloat16, device="cuda")
     got, _, _, _ = run_mx(lay, ws=ws, out=out)
     assert torch.equal(got.view(torch.int16), ref_out.view(torch.int16))
+
+
+# Tiled-path shapes drawn once (numpy seed 2027; H and I multiples of 128)
+# with block_m 64, 128 and 256.
+RANDOM_MX_TILED = [
+    (2501, 64, 2, 1152, 128), (633, 32, 8, 1408, 256), (638, 60, 4, 256, 256),
+    (2974, 60, 2, 256, 384), (518, 32, 2, 896, 128), (2632, 32, 1, 640, 384),
+    (1027, 8, 4, 1152, 256), (1511, 8, 4, 256, 896),
+]
+
+
+@pytest.mark.parametrize("M,E,top_k,H,I", RANDOM_MX_TILED)
+def test_forward_mxfp8_tiled_random_shapes(M, E, top_k, H, I):
+    lay = wl.make_mx_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3700 + M)
+    check_mx(lay, n_tokens=24)

@@ -230,3 +230,53 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         monkeypatch.setattr(mo, "_E4M3_ALL", fn(np.arange(256)))
         monkeypatch.setattr(mo, "_E4M3_GRID", fn(np.arange(0x7F)))
     assert not _battery(), f"planted mistake {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# The GPU tests' acceptance of act quantization decisions that either side
+# could take (tests.helpers.mx_ambiguous_act_choices / mx_boundary_reference):
+# it must find exactly the decisions one rounding step could flip, and it
+# must not accept an output that no such decision explains.
+
+def test_ambiguous_act_choices_finds_the_flippable_element():
+    from tests import helpers as h
+    rng = np.random.default_rng(5)
+    a = rng.normal(size=64)
+    a[0] = 4.0                                    # block 0's scale: 2^(2 - 8)
+    # 68.25 scale units: just above the midpoint of bf16 1.0625 (68 units, a
+    # tie of E4M3 64 and 72 that goes to the even code 64) and 1.0703125
+    # (68.5 units -> 72); one fp32 step either way decides the code
+    a[5] = 1.06640625 * (1.0 + 2.0 ** -20)
+    base_bits = mo.round_to_bf16_via_f32(a)
+    choices = h.mx_ambiguous_act_choices(a)
+    assert choices is not None and len(choices) >= 2
+    flips = [np.flatnonzero(c != mo.widen_bf16(base_bits)) for c in choices[1:]]
+    assert any(list(f) == [5] for f in flips)
+    five = [c[5] for c in choices]
+    assert set(five) == {1.0703125, 1.0625}
+    # the two decisions give different codes
+    assert mo.mx_quantize(choices[0])[0][5] != mo.mx_quantize(choices[1])[0][5]
+
+
+def test_ambiguous_act_choices_ignores_values_far_from_midpoints():
+    from tests import helpers as h
+    v = np.full(32, 1.0)                         # bf16-exact, far from every midpoint
+    v[3] = 2.0
+    assert len(h.mx_ambiguous_act_choices(v)) == 1
+
+
+def test_boundary_reference_rejects_a_planted_error():
+    from tests import helpers as h
+    lay = wl.make_mx_layer("toy", 6, E=4, top_k=2, H=128, I=128, seed=41)
+    toks = np.arange(6)
+    r = mo.route(lay["x"], lay["w_router"], 2, lay["renormalize"], lay.get("logit_bias"))
+    ids, w = r["topk_ids"], r["topk_weights"]
+    ref, _, _ = mo.mx_layer_forward(lay, ids, w, toks)
+    y = ref.copy()
+    y[2, 17] += 0.05 * np.abs(ref).max()        # a wrong element no act decision explains
+    got = h.mx_boundary_reference(lay, ids, w, toks, y, ref)
+    assert np.array_equal(got, ref)
+    with pytest.raises(AssertionError):
+        h.assert_close_outputs(y, got, "planted")
+    # the exact oracle output passes untouched
+    assert np.array_equal(h.mx_boundary_reference(lay, ids, w, toks, ref, ref), ref)
