@@ -288,3 +288,22 @@ def test_forward_tiled_random_shapes(M, E, top_k, H, I):
     assert moe.moe_pick_block_m(M, E, top_k) >= 64
     lay = wl.make_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3600 + M)
     check_forward(lay, n_tokens=32)
+
+
+# Small-batch shapes drawn once (numpy seed 2028; E*H*I <= 1e8, H and I
+# multiples of 8): the weight-streaming kernels (block_m 16) and the
+# per-pair GEMVs (M * top_k * 4 <= E).
+RANDOM_STREAM = [(15, 60, 8, 1600, 472), (16, 32, 1, 2824, 560), (119, 32, 1, 1968, 936),
+                 (111, 16, 1, 584, 1424), (136, 60, 2, 448, 1688), (165, 32, 1, 3984, 24),
+                 (165, 64, 1, 1544, 272), (11, 32, 8, 1368, 1368)]
+RANDOM_PAIR = [(1, 64, 4, 496, 1176), (14, 128, 2, 120, 136), (2, 128, 4, 24, 1040),
+               (5, 256, 2, 1088, 328), (1, 16, 1, 1448, 128), (32, 256, 1, 320, 728)]
+
+
+@pytest.mark.parametrize("M,E,top_k,H,I", RANDOM_STREAM + RANDOM_PAIR)
+def test_forward_small_batch_random_shapes(M, E, top_k, H, I):
+    moe = _moe()
+    B = moe.moe_pick_block_m(M, E, top_k)
+    assert B == (1 if M * top_k * 4 <= E else 16)
+    lay = wl.make_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3800 + M + H)
+    check_forward(lay, n_tokens=32)

@@ -212,3 +212,17 @@ RANDOM_MX_TILED = [
 def test_forward_mxfp8_tiled_random_shapes(M, E, top_k, H, I):
     lay = wl.make_mx_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3700 + M)
     check_mx(lay, n_tokens=24)
+
+
+# Small-batch shapes drawn once (numpy seed 2028; H and I multiples of 128):
+# the streaming MXFP8 kernels (block_m 16) and the per-pair MXFP8 GEMVs.
+RANDOM_MX_SMALL = [(36, 256, 6, 896, 256), (87, 60, 4, 3200, 384), (22, 8, 1, 3456, 384),
+                   (188, 32, 1, 3968, 128), (71, 256, 2, 768, 256), (11, 16, 4, 2304, 640),
+                   (1, 32, 2, 1920, 512), (3, 64, 4, 384, 1024), (1, 32, 2, 1792, 1152),
+                   (5, 32, 1, 1792, 384), (14, 64, 1, 640, 1280)]
+
+
+@pytest.mark.parametrize("M,E,top_k,H,I", RANDOM_MX_SMALL)
+def test_forward_mxfp8_small_batch_random_shapes(M, E, top_k, H, I):
+    lay = wl.make_mx_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3900 + M + H)
+    check_mx(lay, n_tokens=24)

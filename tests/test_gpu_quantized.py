@@ -335,3 +335,21 @@ def test_quantized_graph_replay_matches_eager(name, M, bits, over):
         assert torch.equal(out.view(torch.int16), refs[r].view(torch.int16)), f"replay {r}"
         run(inputs[(r + 1) % 3], eager_out)   # eager work between replays
         torch.cuda.synchronize()
+
+
+# Small-batch shapes drawn once (numpy seed 2028): the streaming quantized
+# GEMMs (H and I multiples of 128) and the per-pair GEMVs (M * top_k * 2 <= E,
+# H and I multiples of 64).
+RANDOM_Q_SMALL = [(5, 32, 6, 256, 1024), (14, 64, 8, 128, 1792), (57, 16, 1, 1408, 1280),
+                  (20, 128, 8, 640, 512), (77, 64, 4, 1024, 1408), (198, 64, 1, 1792, 768),
+                  (28, 256, 1, 448, 832), (16, 256, 8, 448, 448), (8, 60, 1, 384, 832),
+                  (7, 128, 1, 448, 64), (9, 64, 1, 128, 704)]
+
+
+@pytest.mark.parametrize("M,E,top_k,H,I", RANDOM_Q_SMALL)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantized_small_batch_random_shapes(M, E, top_k, H, I, bits):
+    ql = wl.make_quantized_layer("toy", M, bits, E=E, top_k=top_k, H=H, I=I,
+                                 seed=4000 + M + H + bits)
+    assert not tiles(ql)
+    check_quantized(ql, n_tokens=24)
