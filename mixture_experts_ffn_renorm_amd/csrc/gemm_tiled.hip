@@ -153,7 +153,8 @@ struct TileParams {
 };
 
 // QB = 4 or 8: the weights are group-quantized codes (copy-wave tiles,
-// BM = 128 only); see the quantized ring below.
+// BM = 128 only, 16 waves: four more widen the codes into bf16 weight
+// tiles); see the quantized ring below.
 template <int BM, bool kGemm1, bool kMX, bool kPC = false, int QB = 0>
 __global__ __launch_bounds__((QB > 0 ? 1024 : TileCfg<BM, kMX, kPC>::kThreadsT), 1) void gemm_tiled_kernel(
     const TileParams prm) {
