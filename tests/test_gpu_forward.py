@@ -307,3 +307,18 @@ def test_forward_small_batch_random_shapes(M, E, top_k, H, I):
     assert B == (1 if M * top_k * 4 <= E else 16)
     lay = wl.make_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3800 + M + H)
     check_forward(lay, n_tokens=32)
+
+
+def test_forward_maximum_experts_and_top_k():
+    """E = 512 and top_k = 32, the largest the entry points take: the top-k
+    threshold over eight 64-expert blocks, 32 slots per token in the lists and
+    in the per-token sum (256 tokens: 8192 pairs, 16 per expert, block_m 64)."""
+    lay = wl.make_layer("toy", 256, E=512, top_k=32, H=256, I=128, seed=4100)
+    check_forward(lay, n_tokens=32)
+
+
+def test_forward_largest_batch():
+    """65536 tokens of the Qwen3 prefill shape: 524288 pairs, the index lists
+    cut into the maximum number of segments, ~4100 block tiles per GEMM."""
+    lay = wl.make_layer("qwen3_prefill", 65536)
+    check_forward(lay, n_tokens=24)

@@ -226,3 +226,8 @@ RANDOM_MX_SMALL = [(36, 256, 6, 896, 256), (87, 60, 4, 3200, 384), (22, 8, 1, 34
 def test_forward_mxfp8_small_batch_random_shapes(M, E, top_k, H, I):
     lay = wl.make_mx_layer("toy", M, E=E, top_k=top_k, H=H, I=I, seed=3900 + M + H)
     check_mx(lay, n_tokens=24)
+
+
+def test_forward_mxfp8_maximum_experts_and_top_k():
+    lay = wl.make_mx_layer("toy", 256, E=512, top_k=32, H=256, I=128, seed=4200)
+    check_mx(lay, n_tokens=24)

@@ -353,3 +353,9 @@ def test_quantized_small_batch_random_shapes(M, E, top_k, H, I, bits):
                                  seed=4000 + M + H + bits)
     assert not tiles(ql)
     check_quantized(ql, n_tokens=24)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantized_maximum_experts_and_top_k(bits):
+    ql = wl.make_quantized_layer("toy", 256, bits, E=512, top_k=32, H=256, I=128, seed=4300 + bits)
+    check_quantized(ql, n_tokens=24)
