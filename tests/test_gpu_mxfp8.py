@@ -231,3 +231,21 @@ def test_forward_mxfp8_small_batch_random_shapes(M, E, top_k, H, I):
 def test_forward_mxfp8_maximum_experts_and_top_k():
     lay = wl.make_mx_layer("toy", 256, E=512, top_k=32, H=256, I=128, seed=4200)
     check_mx(lay, n_tokens=24)
+
+
+# Degenerate layers: one expert (a dense FFN) and top_k = E, on the
+# streaming kernels and on the tiles.
+@pytest.mark.parametrize("M,E,top_k", [(3, 1, 1), (40, 1, 1), (3, 4, 4), (100, 4, 4)])
+def test_forward_mxfp8_degenerate_layers(M, E, top_k):
+    lay = wl.make_mx_layer("toy", M, E=E, top_k=top_k, H=256, I=128, seed=4600 + M + E)
+    check_mx(lay, n_tokens=24)
+
+
+def test_forward_mxfp8_zero_tokens():
+    import torch
+    moe = _moe()
+    lay = wl.make_mx_layer("toy", 3, E=8, top_k=2, H=256, I=128, seed=4700)
+    x0 = h.dev_bf16(lay["x"])[:0]
+    out, info = moe.moe_forward_mxfp8(x0, h.dev_bf16(lay["w_router"]), mx_to_device(lay), 2, True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256) and info["launches"] == 0

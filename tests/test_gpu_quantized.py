@@ -359,3 +359,28 @@ def test_quantized_small_batch_random_shapes(M, E, top_k, H, I, bits):
 def test_quantized_maximum_experts_and_top_k(bits):
     ql = wl.make_quantized_layer("toy", 256, bits, E=512, top_k=32, H=256, I=128, seed=4300 + bits)
     check_quantized(ql, n_tokens=24)
+
+
+# Degenerate layers: one expert (a dense FFN) and top_k = E (every expert
+# chosen, renormalized weights = the softmax), on the streaming GEMMs (few
+# pairs per expert) and on the tiles.
+DEGENERATE = [(3, 1, 1), (40, 1, 1), (3, 4, 4), (100, 4, 4)]
+
+
+@pytest.mark.parametrize("M,E,top_k", DEGENERATE)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantized_degenerate_layers(M, E, top_k, bits):
+    ql = wl.make_quantized_layer("toy", M, bits, E=E, top_k=top_k, H=256, I=128,
+                                 seed=4400 + M + E + bits)
+    check_quantized(ql, n_tokens=24)
+
+
+def test_quantized_zero_tokens():
+    import torch
+    moe = _moe()
+    ql = wl.make_quantized_layer("toy", 3, 4, E=8, top_k=2, H=256, I=128, seed=4500)
+    x0 = h.dev_bf16(ql["x"])[:0]
+    out, info = moe.moe_forward_quantized(x0, h.dev_bf16(ql["w_router"]), quant_to_device(ql), 2,
+                                          True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256) and info["launches"] == 0
