@@ -322,10 +322,11 @@ typedef struct moe_quantized_weights {
  * info->sorted 1).  The streaming kernels need H and I to be multiples of
  * 128 (other shapes run the per-pair GEMVs there).  Where moe_forward runs
  * its tiles (more than 8 pairs per expert), the quantized layer runs the
- * copy-wave tiles over block_m 128 lists with each stage's codes widened by the copy waves into bf16
- * weight tiles in LDS (w = s*q + b rounded once to bf16, as a quantized
- * matmul in the activation dtype does) and GEMM 2's bf16 pair-order rows
- * summed per token (info->variant MOE_VARIANT_TILED_QUANT).
+ * copy-wave tiles over block_m 128 lists, four more waves per workgroup
+ * widening each stage's codes into bf16 weight tiles in LDS (w = s*q + b
+ * rounded once to bf16, as a quantized matmul in the activation dtype does),
+ * and GEMM 2's bf16 pair-order rows summed per token (info->variant
+ * MOE_VARIANT_TILED_QUANT).
  *
  *   x, w_router, logit_bias, out, topk_ids_out, topk_weights_out, workspace:
  *                as for moe_forward (same workspace size)

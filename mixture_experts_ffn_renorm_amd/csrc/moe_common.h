@@ -531,7 +531,7 @@ bool qgemm_stream_shapes_ok(int H, int I);
 hipError_t launch_qgemm1_stream(const QGemmArgs& a, hipStream_t s);
 hipError_t launch_qgemm2_stream(const QGemmArgs& a, hipStream_t s);
 // The same GEMMs on the copy-wave tiles (block_m 128; H and I multiples of
-// 64): the copy waves widen each stage's codes into bf16 weight tiles in
+// 64): four widen waves turn each stage's codes into bf16 weight tiles in
 // LDS.  GEMM 2 writes bf16 pair-order rows into partial and sums them into out.
 hipError_t launch_qgemm1_tiled(const QGemmArgs& a, hipStream_t s);
 hipError_t launch_qgemm2_tiled(const QGemmArgs& a, hipStream_t s);
