@@ -141,8 +141,8 @@ def stored_traffic(workload_key, kernel):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (multi-GPU sharding is described as design, not built)",
+        print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding over several GPUs is a design, not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
