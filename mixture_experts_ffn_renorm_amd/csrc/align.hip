@@ -48,10 +48,13 @@ __device__ __forceinline__ void count_piece(const int32_t* __restrict__ ids, int
                                             int* hist, int nbits) {
   const int lane = threadIdx.x & 63;
   const unsigned long long below = (1ull << lane) - 1ull;
+  // the next chunk's id is loaded before this chunk's ballots
+  int id_next = s0 + lane < s1 ? ids[s0 + lane] : 0;
   for (int base = s0; base < s1; base += 64) {
     const int p = base + lane;
     const bool valid = p < s1;
-    const int id = valid ? ids[p] : 0;
+    const int id = id_next;
+    id_next = ids[min(p + 64, s1 - 1)];   // unconditional: one load in flight, no branch
     const unsigned long long m = match_lanes(id, valid, nbits);
     if (valid && (m & below) == 0ull) atomicAdd(&hist[id], __popcll(m));
   }
@@ -134,10 +137,18 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
   int n_e = 0, before = 0;
   if (tid < E) {
     if (G > 1) {
-      for (int i = 0; i < G; ++i) {
-        const int c = seg_counts[(size_t)i * E + tid];
-        n_e += c;
-        if (i < gid) before += c;
+      // 16 independent loads in flight per batch: the counts were written
+      // by another launch, so each is a trip past this XCD's L2
+      for (int i0 = 0; i0 < G; i0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] = seg_counts[(size_t)min(i0 + j, G - 1) * E + tid];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int v = i0 + j < G ? c[j] : 0;
+          n_e += v;
+          if (i0 + j < gid) before += v;
+        }
       }
     } else {
       for (int i = 0; i < kWaves; ++i) n_e += hist[i * E + tid];
@@ -169,10 +180,12 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
   // stable scatter, 64 pairs at a time per wave, in pair order
   const unsigned long long below = (1ull << lane) - 1ull;
   int* my_start = hist + w * E;
+  int id_next = sg.w0 + lane < sg.w1 ? ids[sg.w0 + lane] : 0;
   for (int base = sg.w0; base < sg.w1; base += 64) {
     const int p = base + lane;
     const bool valid = p < sg.w1;
-    const int id = valid ? ids[p] : 0;
+    const int id = id_next;
+    id_next = ids[min(p + 64, sg.w1 - 1)];
     const unsigned long long match = match_lanes(id, valid, nbits);
     const int rank = __popcll(match & below);
     const int size = __popcll(match);
