@@ -211,10 +211,13 @@ __device__ __forceinline__ float sum_partials(const float* src, int stride, int 
 // LDS ints used by the index-list build of one segment (1024 threads).
 __host__ __device__ constexpr int align_smem_ints(int E) { return 16 * E + (E + 1) + E + 16; }
 
-// Per-wave LDS floats of topk_token: all logits padded to a multiple of 64
-// (only for the many-ties path), 64 lane maxima, 64 candidate logits, 64
-// candidate ids, 32 slot ids, 32 slot logits.
-__host__ __device__ constexpr int topk_wave_floats(int E) { return ((E + 63) & ~63) + 256; }
+// Per-wave LDS floats of topk_token.  E <= 128: 32 slot ids and 32 slot
+// weights.  Larger E: all logits padded to a multiple of 64 (only for the
+// many-ties path), 64 lane maxima, 64 candidate logits, 64 candidate ids,
+// 32 slot ids, 32 slot logits.
+__host__ __device__ constexpr int topk_wave_floats(int E) {
+  return E <= 128 ? 64 : ((E + 63) & ~63) + 256;
+}
 
 struct TopkSlot {
   int id;     // expert of slot lane (lane < top_k)
@@ -222,6 +225,121 @@ struct TopkSlot {
 };
 
 namespace topk_detail {
+// Order-preserving 32-bit key of a finite logit (or -inf): larger logit,
+// larger key; -0 and +0 get the same key, as they compare equal.  Real keys
+// are >= 0x007fffff (that of -inf), so 0 marks an empty slot.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Number of the wave's keys >= c (uniform).  All compares are issued
+// before the first population count (each ballot lands in its own scalar
+// register pair), so the vector-to-scalar latency is paid once per count,
+// not once per ballot.
+template <int NB>
+__device__ __forceinline__ int count_ge(const uint32_t (&key)[NB], uint32_t c) {
+  unsigned long long m[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) m[i] = __ballot(key[i] >= c);
+  __builtin_amdgcn_sched_group_barrier(0x2, NB, 0);       // the compares (VALU)
+  __builtin_amdgcn_sched_group_barrier(0x4, 2 * NB, 0);   // then the counts (SALU)
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) n += __popcll(m[i]);
+  return n;
+}
+
+// topk_token for E <= 64 NB (NB <= 2); lane l holds logits l, l + 64, ...
+template <int NB>
+__device__ __forceinline__ TopkSlot topk_nb(const float* __restrict__ row, int E, int top_k,
+                                            int renormalize, float* scratch) {
+  const int lane = threadIdx.x & 63;
+  int* s_id = reinterpret_cast<int*>(scratch);   // [32]
+  float* s_w = scratch + 32;                     // [32]
+  float v[NB];
+  uint32_t key[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : 0.f;
+    key[i] = e < E ? order_key(v[i]) : 0u;
+  }
+  // T = the top_k-th largest key: the largest value whose count of keys at
+  // or above it is still >= top_k, built one bit at a time from the top.
+  uint32_t T = 0u;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    if (count_ge(key, c) >= top_k) T = c;
+  }
+  // kept: every key above T, then keys equal to T in expert order until
+  // top_k are kept (exact ties go to the lower expert id)
+  int need = top_k - count_ge(key, T + 1u);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  bool kept[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const unsigned long long eq = __ballot(key[i] == T);
+    kept[i] = key[i] > T || (key[i] == T && __popcll(eq & below) < need);
+    need -= min(__popcll(eq), need);
+  }
+  // slot of a kept expert = kept experts with a larger logit, or the same
+  // logit and a lower id; the largest kept key is the softmax shift
+  int slot[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) slot[i] = 0;
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    for (unsigned long long m = __ballot(kept[j]); m != 0ull; m &= m - 1ull) {
+      const int L = __builtin_ctzll(m);
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key[j], L);
+      const int idj = 64 * j + L;
+      kmax = kj > kmax ? kj : kmax;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        slot[i] += (kj > key[i]) | ((kj == key[i]) & (idj < lane + 64 * i));
+    }
+  }
+  const float mx = key_logit(kmax);
+  float ex[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) ex[i] = __expf(v[i] - mx);
+  float denom = 0.f;
+  if (renormalize) {
+    // the softmax denominator cancels: sum the kept exponentials, in expert order
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      for (unsigned long long m = __ballot(kept[j]); m != 0ull; m &= m - 1ull)
+        denom += __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex[j]), __builtin_ctzll(m)));
+  } else {
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (lane + 64 * i < E) ps += ex[i];
+    denom = wave_sum(ps);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (kept[i]) {
+      s_id[slot[i]] = lane + 64 * i;
+      s_w[slot[i]] = ex[i] / denom;
+    }
+  __builtin_amdgcn_wave_barrier();
+  TopkSlot out{0, 0.f};
+  if (lane < top_k) {
+    out.id = s_id[lane];
+    out.w = s_w[lane];
+  }
+  __builtin_amdgcn_wave_barrier();   // scratch may be reused by the next token
+  return out;
+}
+
 // Adds to r the count of the 16 values at o that beat v: kMode 0 counts
 // o >= v (all of them precede v's own position), 1 counts o > v (all follow
 // it), 2 counts o > v plus equal values at lower positions (jbase + u < own).
@@ -254,28 +372,17 @@ __device__ __forceinline__ int rank_in(const float* o, int n, float v, int own) 
   for (int j = blk + 64; j < n; j += 16) r = count16<1>(o + j, v, j, own, r);
   return r;
 }
-}  // namespace topk_detail
 
-// Router steps for one token, by one wave (page "Mixture of Experts in vLLM
-// - From First Principles to fused_moe", section "One expert, and one
-// token", sub-section "One token uses only 8 experts"): softmax over all E
-// logits, keep the top_k largest in descending order (exact ties -> lower
-// expert id), rescale the kept probabilities to sum 1 if renormalize.
-//
-// Lane l owns logits l, l + 64, ...  The k-th largest of the 64 lane maxima
-// T is a lower bound of the k-th largest logit (k lanes hold a value >= T),
-// so the kept experts are among the candidates >= T, usually little more
-// than k of them.  Candidates are packed in expert order (one ballot per
-// 64-expert block) and each is ranked against the others with broadcast
-// LDS reads (rank = larger logits + equal logits of lower id); rank j < k
-// is slot j.  More than 64 candidates (many exact ties) ranks every logit
-// the same way.  The max is slot 0.  With renormalize the softmax
-// denominator cancels and only the kept exponentials are summed; without
-// it every lane adds its share and a wave sum follows.  E <= 512,
-// top_k <= 32, finite logits.  Returns slot lane's expert and weight on
-// lanes < top_k.
-__device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int top_k,
-                                      int renormalize, float* scratch) {
+// topk_token for E > 128.  Lane l owns logits l, l + 64, ...  The k-th
+// largest of the 64 lane maxima T is a lower bound of the k-th largest
+// logit (k lanes hold a value >= T), so the kept experts are among the
+// candidates >= T, usually little more than k of them.  Candidates are
+// packed in expert order (one ballot per 64-expert block) and each is ranked
+// against the others with broadcast LDS reads (rank = larger logits + equal
+// logits of lower id); rank j < k is slot j.  More than 64 candidates (many
+// exact ties) ranks every logit the same way.  The max is slot 0.
+__device__ inline TopkSlot topk_lanemax(const float* __restrict__ row, int E, int top_k,
+                                        int renormalize, float* scratch) {
   constexpr int kMaxPerLane = 8;
   const int lane = threadIdx.x & 63;
   const int nblk = (E + 63) >> 6;
@@ -298,7 +405,7 @@ __device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int 
   __builtin_amdgcn_wave_barrier();
   int gt = 0;
 #pragma unroll
-  for (int j = 0; j < 64; j += 16) gt = topk_detail::count16<1>(lm + j, lmax, j, lane, gt);
+  for (int j = 0; j < 64; j += 16) gt = count16<1>(lm + j, lmax, j, lane, gt);
   const float T = -wave_max(gt < top_k ? -lmax : -INFINITY);
 
   // pack the candidates in expert order
@@ -321,7 +428,7 @@ __device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int 
     __builtin_amdgcn_wave_barrier();
     const float my = c_v[lane];
     int r = 0;
-    for (int j = 0; j < C; j += 16) r = topk_detail::count16<2>(c_v + j, my, j, lane, r);
+    for (int j = 0; j < C; j += 16) r = count16<2>(c_v + j, my, j, lane, r);
     if (lane < C && r < top_k) {
       s_id[r] = c_id[lane];
       s_l[r] = my;
@@ -334,7 +441,7 @@ __device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int 
     for (int i = 0; i < nblk; ++i) {
       const int e = lane + 64 * i;
       const float vi = lw[e];
-      const int r = topk_detail::rank_in(lw, 64 * nblk, vi, e);
+      const int r = rank_in(lw, 64 * nblk, vi, e);
       if (e < E && r < top_k) {
         s_id[r] = e;
         s_l[r] = vi;
@@ -361,6 +468,35 @@ __device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int 
   }
   __builtin_amdgcn_wave_barrier();   // scratch may be reused by the next token
   return out;
+}
+}  // namespace topk_detail
+
+// Router steps for one token, by one wave (page "Mixture of Experts in vLLM
+// - From First Principles to fused_moe", section "One expert, and one
+// token", sub-section "One token uses only 8 experts"): softmax over all E
+// logits, keep the top_k largest in descending order (exact ties -> lower
+// expert id), rescale the kept probabilities to sum 1 if renormalize.
+//
+// E <= 128 (two logits a lane at most): each logit maps to an
+// order-preserving 32-bit key, and the top_k-th largest key T is found by a
+// 32-step bitwise search whose counts are wave ballots (no LDS, no
+// shuffles).  The kept experts are the keys above T plus the lowest-id keys
+// equal to T; each kept expert's slot is the number of kept experts that
+// precede it (larger logit, or the same logit and a lower id), counted in a
+// scalar loop over the kept set that reads each kept key once.  One LDS
+// round trip moves each kept expert to its slot lane.  Larger E keeps the
+// lane-maxima bound and LDS ranks (topk_lanemax), which measured faster
+// there: the ballot count grows with the logits per lane.
+//
+// With renormalize the softmax denominator cancels and only the kept
+// exponentials are summed; without it every lane adds its share and a wave
+// sum follows.  E <= 512, top_k <= 32, finite logits.  Returns slot lane's
+// expert and weight on lanes < top_k.
+__device__ inline TopkSlot topk_token(const float* __restrict__ row, int E, int top_k,
+                                      int renormalize, float* scratch) {
+  if (E <= 64) return topk_detail::topk_nb<1>(row, E, top_k, renormalize, scratch);
+  if (E <= 128) return topk_detail::topk_nb<2>(row, E, top_k, renormalize, scratch);
+  return topk_detail::topk_lanemax(row, E, top_k, renormalize, scratch);
 }
 
 // Workgroups are handed to the 8 XCDs of the chip round-robin (id % 8).
