@@ -30,22 +30,27 @@ constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTopkWaves = 4;   // tokens per workgroup of the fused top-k + align
 
-// Lanes of the wave whose (valid) id equals this lane's id.
-__device__ __forceinline__ unsigned long long match_lanes(int id, bool valid, int nbits) {
-  unsigned long long m = __ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (id >> b) & 1;
-    const unsigned long long bb = __ballot(valid && bit);
-    m &= bit ? bb : ~bb;
-  }
+// Lanes of the wave whose (valid) id equals this lane's id (ids < 512).
+// All nine bit ballots are taken, whatever E: a bit above E's range is zero
+// in every valid id and leaves the match unchanged.  The compares are all
+// issued before the masks are combined, so the vector-to-scalar latency is
+// paid once.
+__device__ __forceinline__ unsigned long long match_lanes(int id, bool valid) {
+  constexpr int kIdBits = 9;
+  unsigned long long bb[kIdBits];
+  const unsigned long long m0 = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < kIdBits; ++b) bb[b] = __ballot(valid && ((id >> b) & 1));
+  __builtin_amdgcn_sched_group_barrier(0x2, kIdBits + 1, 0);   // the compares first
+  unsigned long long m = m0;
+#pragma unroll
+  for (int b = 0; b < kIdBits; ++b) m &= ((id >> b) & 1) ? bb[b] : ~bb[b];
   return m;
 }
 
-__device__ __forceinline__ int id_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
-
 // Count the experts of pairs [s0, s1) into hist[E] (LDS), one wave.
 __device__ __forceinline__ void count_piece(const int32_t* __restrict__ ids, int s0, int s1,
-                                            int* hist, int nbits) {
+                                            int* hist) {
   const int lane = threadIdx.x & 63;
   const unsigned long long below = (1ull << lane) - 1ull;
   // the next chunk's id is loaded before this chunk's ballots
@@ -55,19 +60,27 @@ __device__ __forceinline__ void count_piece(const int32_t* __restrict__ ids, int
     const bool valid = p < s1;
     const int id = id_next;
     id_next = ids[min(p + 64, s1 - 1)];   // unconditional: one load in flight, no branch
-    const unsigned long long m = match_lanes(id, valid, nbits);
+    const unsigned long long m = match_lanes(id, valid);
     if (valid && (m & below) == 0ull) atomicAdd(&hist[id], __popcll(m));
   }
 }
 
+// Inclusive sum over the lanes of a wave with DPP (no LDS): Hillis-Steele
+// shifts inside each 16-lane row, then row 0's total into row 1 and row 2's
+// into row 3, then the total of rows 0-1 into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);    // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);    // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);    // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);    // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 __device__ __forceinline__ int block_scan_exclusive(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
+  const int incl = wave_inclusive_sum(v);
   if (lane == 63) wave_tot[w] = incl;
   __syncthreads();
   int base = 0;
@@ -105,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void align_count_kernel(
   for (int i = threadIdx.x; i < E; i += kThreads) hist[i] = 0;
   __syncthreads();
   const Seg sg = segment(P, G, blockIdx.x);
-  count_piece(ids, sg.w0, sg.w1, hist, id_bits(E));
+  count_piece(ids, sg.w0, sg.w1, hist);
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += kThreads)
     seg_counts[(size_t)blockIdx.x * E + i] = hist[i];
@@ -125,15 +138,18 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
   int* cnt = boff + E + 1;           // [E]
   int* wave_tot = cnt + E;           // [kWaves]
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int nbits = id_bits(E);
 
   for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
   __syncthreads();
   const Seg sg = segment(P, G, gid);
-  count_piece(ids, sg.w0, sg.w1, hist + w * E, nbits);
+  count_piece(ids, sg.w0, sg.w1, hist + w * E);
   __syncthreads();
 
-  // expert totals, block offsets, start of every (wave, expert) run
+  // expert totals, block offsets, start of every (wave, expert) run; each
+  // expert's 16 wave counts are read once, all in flight together
+  int wc[kWaves];
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) wc[i] = tid < E ? hist[i * E + tid] : 0;
   int n_e = 0, before = 0;
   if (tid < E) {
     if (G > 1) {
@@ -151,7 +167,8 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
         }
       }
     } else {
-      for (int i = 0; i < kWaves; ++i) n_e += hist[i * E + tid];
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) n_e += wc[i];
     }
   }
   const int nb = tid < E ? ceil_div(n_e, B) : 0;
@@ -165,10 +182,10 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
       if (counts_out != nullptr) counts_out[tid] = n_e;
     }
     int run = excl * B + before;
+#pragma unroll
     for (int i = 0; i < kWaves; ++i) {
-      const int c = hist[i * E + tid];
       hist[i * E + tid] = run;
-      run += c;
+      run += wc[i];
     }
   }
   if (tid == 0) {
@@ -186,7 +203,7 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
     const bool valid = p < sg.w1;
     const int id = id_next;
     id_next = ids[min(p + 64, sg.w1 - 1)];
-    const unsigned long long match = match_lanes(id, valid, nbits);
+    const unsigned long long match = match_lanes(id, valid);
     const int rank = __popcll(match & below);
     const int size = __popcll(match);
     int pos = 0;
@@ -200,14 +217,18 @@ __device__ __forceinline__ void align_segment(const int32_t* ids, int P, int E, 
     __builtin_amdgcn_wave_barrier();
   }
 
-  // expert of each block and the pad entries: one wave per expert (waves of
-  // all workgroups), its lanes striding over the expert's blocks and over
-  // the pad slots after its last pair
-  const int gw = gid * kWaves + w, nw = G * kWaves;
+  // expert of each block and the pad entries: one group of lanes per expert
+  // (16 lanes for blocks of up to 16 pairs, else 32 or the whole wave; the
+  // groups of all workgroups' waves share the experts), its lanes striding
+  // over the expert's blocks and over the pad slots after its last pair
+  const int glanes = B <= 16 ? 16 : (B <= 32 ? 32 : 64);
+  const int gpw = 64 / glanes;
+  const int gl = lane & (glanes - 1);
+  const int gw = (gid * kWaves + w) * gpw + lane / glanes, nw = G * kWaves * gpw;
   for (int e = gw; e < E; e += nw) {
     const int b0 = boff[e], b1 = boff[e + 1];
-    for (int blk = b0 + lane; blk < b1; blk += 64) expert_ids[blk] = e;
-    for (int pos = b0 * B + cnt[e] + lane; pos < b1 * B; pos += 64) sorted[pos] = P;
+    for (int blk = b0 + gl; blk < b1; blk += glanes) expert_ids[blk] = e;
+    for (int pos = b0 * B + cnt[e] + gl; pos < b1 * B; pos += glanes) sorted[pos] = P;
   }
 }
 
