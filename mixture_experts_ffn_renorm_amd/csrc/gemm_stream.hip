@@ -430,17 +430,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
 
 // out[t, h] = bf16(sum over slots j of partial[t*top_k + j, h]), j ascending.
 // Page "Mixture of Experts in vLLM ...", section "Put the results back, and
-// combine them per token".  Thread: 4 consecutive columns of one token.
+// combine them per token".  Thread: 4 consecutive columns of one token; all
+// top_k loads are issued before the first add (one memory round trip, not
+// top_k of them).
 __global__ __launch_bounds__(256) void combine_partials_kernel(const float* __restrict__ partial,
                                                                int M, int top_k, int H,
                                                                uint16_t* __restrict__ out) {
+  constexpr int kMaxK = 32;
   const int h4 = H / 4;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long long)M * h4) return;
   const int t = (int)(i / h4), h = (int)(i - (long long)t * h4) * 4;
   const float* src = partial + (size_t)t * top_k * H + h;
-  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
-  for (int j = 1; j < top_k; ++j) sum += *reinterpret_cast<const f32x4*>(src + (size_t)j * H);
+  f32x4 part[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < top_k) part[j] = *reinterpret_cast<const f32x4*>(src + (size_t)j * H);
+  f32x4 sum = part[0];
+#pragma unroll
+  for (int j = 1; j < kMaxK; ++j)
+    if (j < top_k) sum += part[j];
   u32x2 v;
   v[0] = pack_bf16x2(sum[0], sum[1]);
   v[1] = pack_bf16x2(sum[2], sum[3]);

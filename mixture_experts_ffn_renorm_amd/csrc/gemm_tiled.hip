@@ -771,18 +771,30 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __res
   if (i >= (long long)M * h8) return;
   const int t = (int)(i / h8), h = (int)(i - (long long)t * h8) * 8;
   const uint16_t* src = rows + (size_t)t * top_k * H + h;
+  // all top_k row loads leave before the first add
+  constexpr int kMaxK = 32;
+  u32x4 part[kMaxK];
+  float wt[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < top_k) {
+      part[j] = *reinterpret_cast<const u32x4*>(src + (size_t)j * H);
+      wt[j] = topk_weights[(size_t)t * top_k + j];
+    }
   float sum[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) sum[q] = 0.f;
-  for (int j = 0; j < top_k; ++j) {
-    const float w = topk_weights[(size_t)t * top_k + j];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)j * H);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      sum[2 * q] += w * __uint_as_float(v[q] << 16);
-      sum[2 * q + 1] += w * __uint_as_float(v[q] & 0xffff0000u);
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < top_k) {
+      const float w = wt[j];
+      const u32x4 v = part[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sum[2 * q] += w * __uint_as_float(v[q] << 16);
+        sum[2 * q + 1] += w * __uint_as_float(v[q] & 0xffff0000u);
+      }
     }
-  }
   u32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(sum[2 * q], sum[2 * q + 1]);
