@@ -212,6 +212,47 @@ def test_route_exact_ties_across_lane_blocks():
     assert np.array_equal(ids[ok], ref["topk_ids"][ok])
 
 
+TIED128 = [3, 63, 64, 100, 127]
+
+
+@pytest.mark.parametrize("M", [1, 8, 64, 300])
+def test_route_exact_ties_two_logits_a_lane(M):
+    """Up to 128 experts the top-k searches order-preserving keys with wave
+    ballots; experts 3, 63, 64, 100 and 127 share one router row (inside one
+    64-expert block and across the two), so their logits tie exactly and
+    must come out in ascending id order, with the oracle's ids where the
+    margin is clear.  M = 300 reaches the tiled router."""
+    lay = wl.make_layer("qwen3_decode", M, I=8)
+    row = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(lay["w_router"][17]) * 4.0)
+    for e in TIED128:
+        lay["w_router"][e] = row
+    ids, _, logits = run_route(lay)
+    assert len({logits[0, e] for e in TIED128}) == 1
+    ref = mo.route(lay["x"], lay["w_router"], lay["top_k"], True, None)
+    full = 0
+    for t in range(M):
+        r = ids[t].tolist()
+        tied = [e for e in r if e in TIED128]
+        assert tied == sorted(tied)
+        if r[:5] == TIED128:
+            full += 1
+            assert ref["topk_ids"][t][:5].tolist() == TIED128
+    if M >= 8:
+        assert full >= M // 8
+    ok = ref["margin"] > h.MARGIN
+    assert np.array_equal(ids[ok], ref["topk_ids"][ok])
+
+
+@pytest.mark.parametrize("E", [63, 64, 65, 127, 128, 129])
+def test_route_expert_counts_at_the_top_k_split(E):
+    """Expert counts on both sides of the one- and two-logits-a-lane forms
+    and of the lane-maxima form above 128 experts."""
+    for M in (3, 40):
+        check_route(wl.make_layer("qwen15", M, E=E, top_k=8, H=256, I=8, seed=E * 7 + M))
+        check_route(wl.make_layer("qwen15", M, E=E, top_k=8, H=256, I=8, seed=E * 7 + M),
+                    renormalize=False)
+
+
 @pytest.mark.parametrize("name,M", [("wide256", 16), ("qwen3_decode", 8), ("toy", 3)])
 def test_route_all_logits_equal(name, M):
     """A zero router makes every logit 0: the kept experts are 0..k-1 in
