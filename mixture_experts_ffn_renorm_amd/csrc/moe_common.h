@@ -184,10 +184,23 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
   return v;
 }
+// The sum runs on DPP (no LDS round trips): Hillis-Steele shifts inside each
+// 16-lane row, then row 0's total into row 1 and row 2's into row 3, then
+// rows 0-1 into rows 2 and 3; lane 63 ends with the total, which every lane
+// reads.  A fixed order: bitwise repeatable.
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ __forceinline__ float dpp_shifted_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xf, kBound);
+  return v + __builtin_bit_cast(float, s);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  v = dpp_shifted_add<0x111, 0xf, true>(v);    // row_shr:1
+  v = dpp_shifted_add<0x112, 0xf, true>(v);    // row_shr:2
+  v = dpp_shifted_add<0x114, 0xf, true>(v);    // row_shr:4
+  v = dpp_shifted_add<0x118, 0xf, true>(v);    // row_shr:8
+  v = dpp_shifted_add<0x142, 0xa, false>(v);   // row_bcast:15
+  v = dpp_shifted_add<0x143, 0xc, false>(v);   // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Sum of the top_k fp32 partial rows of one token at one column, in slot
