@@ -193,13 +193,21 @@ __device__ __forceinline__ float dpp_shifted_add(float v) {
   const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xf, kBound);
   return v + __builtin_bit_cast(float, s);
 }
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over each group of kLanes consecutive lanes (16, 32 or 64), valid in
+// the group's last lane.
+template <int kLanes>
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(kLanes == 16 || kLanes == 32 || kLanes == 64, "lane group");
   v = dpp_shifted_add<0x111, 0xf, true>(v);    // row_shr:1
   v = dpp_shifted_add<0x112, 0xf, true>(v);    // row_shr:2
   v = dpp_shifted_add<0x114, 0xf, true>(v);    // row_shr:4
   v = dpp_shifted_add<0x118, 0xf, true>(v);    // row_shr:8
-  v = dpp_shifted_add<0x142, 0xa, false>(v);   // row_bcast:15
-  v = dpp_shifted_add<0x143, 0xc, false>(v);   // row_bcast:31
+  if (kLanes >= 32) v = dpp_shifted_add<0x142, 0xa, false>(v);   // row_bcast:15
+  if (kLanes == 64) v = dpp_shifted_add<0x143, 0xc, false>(v);   // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum_last<64>(v);
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 

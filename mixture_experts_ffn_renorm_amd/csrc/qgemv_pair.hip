@@ -256,13 +256,11 @@ __global__ __launch_bounds__(64 * kQMaxWaves) void qgemv_w2_sum_kernel(
 #pragma unroll
     for (int r = 0; r < kRows; ++r) acc[r] = __builtin_fmaf(wt, s[r], acc[r]);
   }
-  // sum over the lanes of each column group (xor offsets stay inside it)
+  // sum over the lanes of each column group (DPP, total in its last lane)
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    float v = acc[r];
-#pragma unroll
-    for (int d = kLanes / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    if (ll == 0) red[w][half * kRows + r] = v;
+    const float v = group_sum_last<kLanes>(acc[r]);
+    if (ll == kLanes - 1) red[w][half * kRows + r] = v;
   }
   __syncthreads();
   if (threadIdx.x < kQ2Cols) {
