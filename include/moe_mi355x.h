@@ -191,8 +191,8 @@ int moe_grouped_gemm_w13_act(const uint16_t* x, const uint16_t* w13,
  *   w2           [E, H, I] bf16
  *   topk_weights [M*top_k] fp32
  *   out          out [M, H] bf16 in token order
- *   workspace    holds the pair-order product [M*top_k, H] (block_m 1:
- *                fp32, already scaled by topk_weights; 16, 64, 128, 256:
+ *   workspace    holds the pair-order product [M*top_k, H] (block_m 1 and
+ *                16: fp32, already scaled by topk_weights; 64, 128, 256:
  *                bf16, scaled in the sum), ws_bytes >= moe_workspace_size(M,
  *                E, top_k, H, I)
  * A second kernel adds each token's top_k rows in slot order in fp32 and

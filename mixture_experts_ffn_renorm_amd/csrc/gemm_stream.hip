@@ -9,12 +9,12 @@
 // block and 32 weight rows:
 //   GEMM 1: 16 gate rows and the matching 16 up rows of W13[e] -> 16 act
 //           columns (SiLU(gate) * up), rows p of act in pair order;
-//   GEMM 2: 64 rows of W2[e] -> 64 output columns; the epilogue stores the
-//           bf16 pair-order row p (the page's cache3), and a second small
-//           kernel adds each token's top_k rows, scaled by topk_weights, in
-//           slot order and writes bf16 (page sections "The rest of the layer
-//           stays in pair order" and "Put the results back, and combine them
-//           per token"); see the GEMM 2 notes below.
+//   GEMM 2: 64 rows of W2[e] -> 64 output columns; the epilogue scales by
+//           topk_weights[p] and stores the fp32 partial row p, and a second
+//           small kernel adds each token's top_k partial rows in slot order
+//           and writes bf16 (page sections "The rest of the layer stays in
+//           pair order" and "Put the results back, and combine them per
+//           token"); see the GEMM 2 notes below.
 //
 // Persistent workgroups (two per CU) walk the tiles; each XCD takes one
 // contiguous range of tiles, so the tiles of one block (same gathered rows)
@@ -94,7 +94,7 @@ struct StreamParams {
   const float* topk_weights;  // GEMM 2
   int M, top_k, E, H, I;
   uint16_t* out;              // GEMM 1: act; GEMM 2: out [M, H]
-  float* partial;             // GEMM 2: [P, H] pair-order rows (bf16 bits)
+  float* partial;             // GEMM 2: [P, H] fp32 weighted partial rows
 };
 
 template <bool kMX>
@@ -259,17 +259,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_kernel(StreamParams 
 // tile boundaries and a tile's combine epilogue runs while the next tile's
 // first slices are in flight; the ring is drained only where the block
 // changes.  Epilogue: each lane stores its four columns of the tile (64
-// columns x 16 pairs) straight from its MFMA registers as bf16 rows
-// p = W2[e] act[p] (8 bytes a lane) -- no LDS staging and no barrier, so
-// the next slices' copies keep streaming.  (Measured at 64 tokens with fp32
-// pre-weighted rows: the kernel ran ~67 us against ~59 us for the same ring
-// streaming the same bytes with no compute, and dropping the 4 MB of
-// row stores recovered ~5 us, while LDS staging, barriers, deferring the
-// stores to the end of the run, and streaming across block boundaries
-// changed nothing; bf16 rows halve those stores: 69.9 -> 66.8 us.)  The
-// per-token sum is the tiled path's combine kernel (at these batch sizes the
-// rows are a few MB, while an in-kernel last-arrival combine costs each tile
-// three serialized memory round trips).
+// columns x 16 pairs) straight from its MFMA registers as fp32 partial rows
+// p = topk_weights[p] * (W2[e] act[p]) -- no LDS staging and no barrier, so
+// the next slices' copies keep streaming.  (Measured at 64 tokens: the
+// kernel runs ~67 us against ~59 us for the same ring streaming the same
+// bytes with no compute; dropping the 4 MB of partial-row stores recovers
+// ~5 us, while LDS staging, barriers, deferring the stores to the end of
+// the run, and streaming across block boundaries changed nothing.)  The
+// per-token sum is the small combine kernel below (at these batch sizes the
+// partial rows are a few MB, while an in-kernel last-arrival combine costs
+// each tile three serialized memory round trips).
 namespace ring2 {
 
 constexpr int kBM = 16;
@@ -295,6 +294,7 @@ template <bool kMX>
 __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams prm) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ int s_pair[kBM];
+  __shared__ float s_wt[kBM];
   __shared__ int s_e;
   constexpr int kSB = stage_bytes<kMX>();
 
@@ -323,6 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
     if (tid < kBM) {
       const int p = prm.sorted[b * kBM + tid];
       s_pair[tid] = p;
+      s_wt[tid] = p < P ? prm.topk_weights[p] : 0.f;
     }
     if (tid == kBM) s_e = prm.expert_ids[b];
     __syncthreads();
@@ -418,12 +419,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_ring_kernel(StreamParams pr
       const int nt = nt0 + g / ns;
       const int p = s_pair[r16];
       const int h = nt * kWRows + wv * 16 + 4 * kg;   // H % 8 == 0: all four exist or none
-      if (p < P && h < H) {
-        u32x2 v;
-        v[0] = pack_bf16x2(acc[0], acc[1]);
-        v[1] = pack_bf16x2(acc[2], acc[3]);
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(prm.partial) + (size_t)p * H + h) = v;
-      }
+      if (p < P && h < H)
+        *reinterpret_cast<f32x4*>(prm.partial + (size_t)p * H + h) = s_wt[r16] * acc;
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     t = run_end;
@@ -520,8 +517,7 @@ hipError_t launch_gemm2(const moe_host::GemmArgs& a, hipStream_t s) {
                      kRing, s, prm);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return moe_host::launch_combine_rows(reinterpret_cast<const uint16_t*>(a.partial),
-                                      a.topk_weights, a.M, a.top_k, a.H, a.out, s);
+  return moe_host::launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
 }
 
 }  // namespace

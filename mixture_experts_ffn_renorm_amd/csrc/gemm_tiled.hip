@@ -891,7 +891,10 @@ hipError_t launch_qgemm2_tiled(const QGemmArgs& q, hipStream_t s) {
   const hipError_t err = q.bits == 4 ? launch_tiled<128, false, false, true, 4>(a, s, rows, &q)
                                      : launch_tiled<128, false, false, true, 8>(a, s, rows, &q);
   if (err != hipSuccess) return err;
-  return launch_combine_rows(rows, q.topk_weights, q.M, q.top_k, q.H, q.out, s);
+  const long long n8 = (long long)q.M * (q.H / 8);
+  hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, rows,
+                     q.topk_weights, q.M, q.top_k, q.H, q.out);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
@@ -906,14 +909,9 @@ hipError_t launch_gemm2_tiled(const GemmArgs& a, hipStream_t s) {
           : a.block_m == 128 ? launch_tiled<128, false, false, true>(a, s, rows)
                              : launch_tiled<64, false, false, true>(a, s, rows);
   if (err != hipSuccess) return err;
-  return launch_combine_rows(rows, a.topk_weights, a.M, a.top_k, a.H, a.out, s);
-}
-
-hipError_t launch_combine_rows(const uint16_t* rows, const float* topk_weights, int M, int top_k,
-                               int H, uint16_t* out, hipStream_t s) {
-  const long long n8 = (long long)M * (H / 8);
+  const long long n8 = (long long)a.M * (a.H / 8);
   hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, rows,
-                     topk_weights, M, top_k, H, out);
+                     a.topk_weights, a.M, a.top_k, a.H, a.out);
   return hipGetLastError();
 }
 

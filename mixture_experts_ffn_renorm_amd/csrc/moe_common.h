@@ -604,10 +604,6 @@ hipError_t launch_gemm2_stream(const GemmArgs& a, hipStream_t s);
 // out[t] = bf16(sum over slots j of partial[t*top_k + j]), j ascending.
 hipError_t launch_combine_partials(const float* partial, int M, int top_k, int H, uint16_t* out,
                                    hipStream_t s);
-// out[t] = bf16(sum over slots j of topk_weights[t, j] * rows[t*top_k + j]),
-// rows bf16 [M*top_k, H] in pair order (H % 8 == 0).
-hipError_t launch_combine_rows(const uint16_t* rows, const float* topk_weights, int M, int top_k,
-                               int H, uint16_t* out, hipStream_t s);
 
 // Per-pair GEMVs of very small batches: GEMV 1 writes act [P, I]; GEMV 2
 // multiplies, weights and sums each token's top_k rows straight into

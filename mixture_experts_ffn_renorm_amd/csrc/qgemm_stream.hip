@@ -32,8 +32,8 @@
 // the non-temporal policy).  Every wave issues the same number of copies
 // per slice, so one vmcnt count serves all.  Pads (id >= M*top_k) and the
 // K tail copy the zeroed page, whose codes, scales and biases are all zero.
-// GEMM 1 stores SiLU(gate) * up as bf16 act; GEMM 2 stores its tile as
-// bf16 pair-order rows, which the per-token sum scales and adds.  H and I must be multiples of 128
+// GEMM 1 stores SiLU(gate) * up as bf16 act; GEMM 2 stores topk_weights[p]
+// times its tile as fp32 partial rows.  H and I must be multiples of 128
 // (the 4-byte scale copies stay aligned); other shapes run the per-pair
 // GEMVs.
 #include <algorithm>
@@ -102,7 +102,7 @@ struct QStreamParams {
   const float* topk_weights;    // GEMM 2
   int M, top_k, E, H, I;
   uint16_t* out;                // GEMM 1: act [P, I]
-  float* partial;               // GEMM 2: [P, H] pair-order rows (bf16 bits)
+  float* partial;               // GEMM 2: [P, H] fp32 weighted rows
 };
 
 // A tile is one block (16 pairs) and 128 weight rows: GEMM 1 the 64 gate
@@ -139,11 +139,12 @@ __device__ __forceinline__ int cslot(int R, int c) { return c ^ ((R >> 1) & 7); 
 __device__ __forceinline__ int aslot(int R, int c) { return c ^ (R & 15); }
 
 // kG1: GEMM 1 (x rows, SiLU(gate) * up into act) or GEMM 2 (act rows,
-// bf16 pair-order rows).
+// weighted fp32 partial rows).
 template <int BITS, bool kG1>
 __global__ __launch_bounds__(kThreads, 2) void qgemm_stream_kernel(QStreamParams prm) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ int s_pair[kBM];
+  __shared__ float s_wt[kBM];
   constexpr int kSB = stage_bytes<BITS>();
   constexpr int kKS = kslice<BITS>();
   constexpr int kG = groups<BITS>();
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void qgemm_stream_kernel(QStreamParams
     if (tid < kBM) {
       const int p = prm.sorted[b * kBM + tid];
       s_pair[tid] = p;
+      if (!kG1) s_wt[tid] = p < P ? prm.topk_weights[p] : 0.f;
     }
     __syncthreads();
 
@@ -326,17 +328,12 @@ __global__ __launch_bounds__(kThreads, 2) void qgemm_stream_kernel(QStreamParams
         v[1] = pack_bf16x2(silu_mul(acc0[2], acc1[2]), silu_mul(acc0[3], acc1[3]));
         *reinterpret_cast<u32x2*>(prm.out + (size_t)p * I + nt * 64 + T0 + 4 * kg) = v;
       } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(prm.partial) + (size_t)p * H + nt * kWR + 4 * kg;
-        u32x2 v0, v1;
-        v0[0] = pack_bf16x2(acc0[0], acc0[1]);
-        v0[1] = pack_bf16x2(acc0[2], acc0[3]);
-        v1[0] = pack_bf16x2(acc1[0], acc1[1]);
-        v1[1] = pack_bf16x2(acc1[2], acc1[3]);
-        *reinterpret_cast<u32x2*>(dst + T0) = v0;
-        *reinterpret_cast<u32x2*>(dst + T1) = v1;
+        float* dst = prm.partial + (size_t)p * H + nt * kWR + 4 * kg;
+        *reinterpret_cast<f32x4*>(dst + T0) = s_wt[r16] * acc0;
+        *reinterpret_cast<f32x4*>(dst + T1) = s_wt[r16] * acc1;
       }
     }
-    __syncthreads();   // s_pair and the ring are reused by the next tile
+    __syncthreads();   // s_pair, s_wt and the ring are reused by the next tile
   }
 }
 
@@ -396,8 +393,7 @@ hipError_t launch_q2(const moe_host::QGemmArgs& a, hipStream_t s) {
                      kRing, s, prm);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return moe_host::launch_combine_rows(reinterpret_cast<const uint16_t*>(a.partial),
-                                      a.topk_weights, a.M, a.top_k, a.H, a.out, s);
+  return moe_host::launch_combine_partials(a.partial, a.M, a.top_k, a.H, a.out, s);
 }
 
 }  // namespace
