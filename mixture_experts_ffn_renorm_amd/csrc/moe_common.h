@@ -206,6 +206,20 @@ __device__ __forceinline__ float group_sum_last(float v) {
   if (kLanes == 64) v = dpp_shifted_add<0x143, 0xc, false>(v);   // row_bcast:31
   return v;
 }
+// Maximum over each 16-lane row, in every lane of the row (DPP: swap
+// neighbours, swap pairs, mirror each half row, mirror the row).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max_with(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false);
+  return __builtin_fmaxf(v, __builtin_bit_cast(float, s));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_max_with<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+  v = dpp_max_with<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_max_with<0x141>(v);   // row_half_mirror
+  v = dpp_max_with<0x140>(v);   // row_mirror
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v = group_sum_last<64>(v);
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));

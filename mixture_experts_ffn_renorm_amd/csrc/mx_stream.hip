@@ -184,8 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm1_stream_mxq_kernel(MxqParams
       const float v0 = bf16_round(silu_mul(g[q], u[q]));
       const float v1 = bf16_round(silu_mul(g[q + 1], u[q + 1]));
       float amax = __builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, d, kWave));
+      amax = row16_max(amax);   // the 16 threads of pair pr are one DPP row
       const int shared = mx_shared_exp(amax);
       const int p = s_pair[pr];
       if (p < P) {

@@ -307,3 +307,49 @@ def test_forward_index_lists_bit_exact(M):
     assert np.array_equal(cnt.cpu().numpy(), ref["expert_counts"])
     assert np.array_equal(e.cpu().numpy()[:nb], ref["expert_ids"])
     assert np.array_equal(s.cpu().numpy()[:nb * B], ref["sorted_token_ids"])
+
+
+def _random_list_cases(n: int = 14, seed: int = 2024):
+    """(M, E, top_k) drawn so the lists are built (M * top_k * 4 > E), half of
+    them one-segment batches (the fused top-k + lists launch, P <= 2048) and
+    half multi-segment ones, over every top-k form (E up to 512, k up to 32)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([2, 7, 60, 64, 65, 128, 129, 200, 256, 512]))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        lo = E // (4 * k) + 1
+        if i % 2 == 0:
+            M = int(rng.integers(lo, max(lo, 2048 // k) + 1))
+        else:
+            M = int(rng.integers(2048 // k + 1, 2048 // k + 600))
+        cases.append((M, E, k))
+    return cases
+
+
+@pytest.mark.parametrize("M,E,k", _random_list_cases())
+def test_forward_index_lists_random_shapes(M, E, k):
+    """moe_forward's own lists against oracle.align of its topk_ids, bit for
+    bit, on random expert counts, top_k and batch sizes."""
+    import torch
+    moe = _moe()
+    lay = wl.make_layer("qwen15", M, E=E, top_k=k, H=64, I=64, seed=M * 131 + E * 7 + k)
+    H, I = lay["H"], lay["I"]
+    d = h.layer_to_device(lay)
+    ws = moe.workspace(M, E, k, H, I)
+    ws.fill_(0xFF)
+    ids = torch.full((M, k), -1, dtype=torch.int32, device="cuda")
+    print(f"index lists case M={M} E={E} k={k}", flush=True)
+    _, info = moe.moe_forward(d["x"], d["w_router"], d["w13"], d["w2"], k, True,
+                              topk_ids_out=ids, ws=ws)
+    torch.cuda.synchronize()
+    assert info["sorted"] == 1
+    s, e, off, cnt, B = moe.forward_lists(ws, M, E, k, H, I)
+    assert B == info["block_m"]
+    ref = mo.align(ids.cpu().numpy(), E, B)
+    off = off.cpu().numpy()
+    nb = int(off[E])
+    assert np.array_equal(off, ref["expert_block_offsets"])
+    assert np.array_equal(cnt.cpu().numpy(), ref["expert_counts"])
+    assert np.array_equal(e.cpu().numpy()[:nb], ref["expert_ids"])
+    assert np.array_equal(s.cpu().numpy()[:nb * B], ref["sorted_token_ids"])
