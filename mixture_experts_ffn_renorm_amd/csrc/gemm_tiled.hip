@@ -738,6 +738,10 @@ __global__ __launch_bounds__((QB > 0 ? 1024 : TileCfg<BM, kMX, kPC>::kThreadsT),
       }
     } else {
       if (QB > 0) barrier_nofence();   // barrier -1 (the widen waves start stage 0)
+      // bf16 GEMM 1: the MFMA waves take issue priority over the copy wave
+      // of their SIMD (measured: GEMM 1 2-4 % faster; GEMM 2, the MXFP8 and
+      // the quantized tiles gain nothing)
+      if constexpr (kGemm1 && QB == 0 && !kMX) __builtin_amdgcn_s_setprio(1);
       for (int g = 0; g < G; ++g) {
         barrier_nofence();
         consume();
