@@ -589,3 +589,18 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(mo, attr, fn)
     assert not _battery(), f"planted mistake {name} passed every pin"
+
+
+def test_route_zero_logits_from_signed_zero_rows_tie_by_lower_id():
+    """A router row of -0 weights and a row of +0 weights both score a token
+    exactly zero (the sum of signed-zero products is a zero), so the two
+    experts tie and the lower id comes first, in either order of the rows;
+    experts 2 and 3 score below zero."""
+    H = 8
+    x = wl.f32_to_bf16_bits(np.full((1, H), 0.5, dtype=np.float32))
+    rows = np.array([[-0.0] * H, [0.0] * H, [-1.0] * H, [-2.0] * H], dtype=np.float32)
+    for perm in ([0, 1, 2, 3], [1, 0, 2, 3]):
+        r = mo.route(x, wl.f32_to_bf16_bits(rows[perm]), 2, True)
+        assert r["logits_f32"][0, 0] == 0.0 and r["logits_f32"][0, 1] == 0.0
+        assert r["topk_ids"][0].tolist() == [0, 1]
+        assert np.allclose(r["topk_weights"][0], [0.5, 0.5])
