@@ -353,3 +353,18 @@ def test_forward_index_lists_random_shapes(M, E, k):
     assert np.array_equal(cnt.cpu().numpy(), ref["expert_counts"])
     assert np.array_equal(e.cpu().numpy()[:nb], ref["expert_ids"])
     assert np.array_equal(s.cpu().numpy()[:nb * B], ref["sorted_token_ids"])
+
+
+def test_route_zero_logits_from_signed_zero_rows():
+    """Router rows of -0 and of +0 weights both score zero: the GPU keeps the
+    lower expert id first, in either order of the rows, as the oracle does."""
+    H = 64
+    x = wl.f32_to_bf16_bits(np.full((3, H), 0.5, dtype=np.float32))
+    rows = np.array([[-0.0] * H, [0.0] * H, [-1.0] * H, [-2.0] * H], dtype=np.float32)
+    for perm in ([0, 1, 2, 3], [1, 0, 2, 3]):
+        lay = {"x": x, "w_router": wl.f32_to_bf16_bits(rows[perm]), "top_k": 2,
+               "renormalize": True}
+        ids, wts, logits = run_route(lay)
+        assert np.all(logits[:, :2] == 0.0)
+        assert ids.tolist() == [[0, 1]] * 3
+        assert np.abs(wts - 0.5).max() <= 1e-6
